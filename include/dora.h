@@ -1,0 +1,166 @@
+/*
+ * dora.h - C ABI of the MI355X (gfx950) DoRA hot-path library, libdora.so.
+ *
+ * DoRA rescales every output row of an adapted weight to a learned magnitude:
+ *
+ *     V' = W0 + s * B A            (adapted direction, [d_out, d_in])
+ *     n_i = || V'_i ||             (row norm, one per output feature)
+ *     y   = x (diag(m / n) V')^T   (layer output)
+ *
+ * (DoRA reading notes, zhongzhuzhou.org: Sec. 3.1 eq. (6) and Sec. 3.2
+ * Algorithm 1 steps 7-11; Scaling DoRA summary page, gptget.net, arXiv
+ * 2603.22276, abstract, for the row-wise norm of W + sBA and the scale s.)
+ *
+ * The library never forms the d_out x d_in product B A.  The norm is
+ * evaluated in factored form from ||W0_i||^2, 2s B_i.(W0 A^T)_i and
+ * s^2 B_i (A A^T) B_i^T (Scaling DoRA abstract: base, cross and Gram terms),
+ * and the output is composed in one pass in the near-unity form
+ * y = base + ((g - 1) base + g s lora) with g - 1 = (m - n) / n
+ * (Scaling DoRA abstract: numerically stable form for the near-unity regime).
+ *
+ * Conventions for every entry point
+ *   Layout     Row-major and contiguous, nn.Linear convention:
+ *                W0 [d_out, d_in]   A [r, d_in]   B [d_out, r]   m [d_out]
+ *                x  [T, d_in]       y [T, d_out]  xs [T, r]      (T = tokens)
+ *   Types      Every tensor has the layer dtype (DORA_F32 or DORA_BF16), except
+ *              norm and grad_m, which are always float32.  Accumulation is
+ *              float32; each output is rounded once, to nearest even.
+ *   Memory     All tensor pointers are DEVICE pointers, 16-byte aligned.  The
+ *              caller owns every buffer, including the workspace `ws`; the
+ *              library allocates no device memory and keeps no state between
+ *              calls.  Inputs are read only.  Outputs must not overlap inputs
+ *              or each other.
+ *   Streams    Work is enqueued on `hip_stream` (a hipStream_t; NULL = the
+ *              null stream) and the call returns without synchronising.  Calls
+ *              on distinct buffers may be made from several host threads.
+ *   Errors     Arguments are validated before anything is enqueued; on a
+ *              validation error nothing is written.  Return value 0 = enqueued,
+ *              negative = DORA_ERR_* below.  DORA_ERR_HIP means the HIP runtime
+ *              rejected a launch (hipGetLastError is checked after each one);
+ *              kernels already enqueued may then have run.
+ *   Sizes      d_out, d_in >= 1; r >= 0; tokens >= 0.  d_out, d_in and r must
+ *              be multiples of 8 (16-byte rows for both dtypes).  Every
+ *              element count must stay below 2^31 per tensor row-block and
+ *              2^62 in total.
+ */
+#ifndef DORA_H
+#define DORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DORA_API __attribute__((visibility("default")))
+
+typedef enum { DORA_F32 = 0, DORA_BF16 = 1 } dora_dtype;
+
+/* Layer description shared by every call. */
+typedef struct {
+    int64_t  d_out;     /* output features (rows of W0, B; entries of m)        */
+    int64_t  d_in;      /* input features (columns of W0, A; columns of x)      */
+    int64_t  r;         /* LoRA rank (rows of A, columns of B); 0 = no LoRA     */
+    int64_t  tokens;    /* T, rows of x and y; 0 allowed                        */
+    int32_t  dtype;     /* dora_dtype of every tensor except norm / grad_m      */
+    float    s;         /* LoRA scale multiplying B A (any finite value)        */
+    uint32_t flags;     /* DORA_FLAG_* bits, 0 for the default path             */
+    uint32_t reserved;  /* must be 0                                            */
+} dora_shape;
+
+/* flags */
+#define DORA_FLAG_EXACT_NORM_GRAD   (1u << 0)  /* backward: undetached norm gradient (DoRA reading notes, Appendix A.1) */
+#define DORA_FLAG_SEPARATE_COMPOSE  (1u << 1)  /* forward/backward: run the standalone compose kernels instead of the GEMM-fused ones */
+
+/* op ids for dora_workspace_bytes */
+#define DORA_OP_NORM      0
+#define DORA_OP_FORWARD   1
+#define DORA_OP_BACKWARD  2
+
+/* return codes */
+#define DORA_OK              0
+#define DORA_ERR_NULL       -1  /* a required pointer is NULL                          */
+#define DORA_ERR_SHAPE      -2  /* a dimension is out of range or not a multiple of 8   */
+#define DORA_ERR_DTYPE      -3  /* dtype is not DORA_F32 / DORA_BF16                    */
+#define DORA_ERR_ALIGN      -4  /* a pointer is not 16-byte aligned                     */
+#define DORA_ERR_WORKSPACE  -5  /* ws_bytes < dora_workspace_bytes(shape, op)           */
+#define DORA_ERR_HIP        -6  /* the HIP runtime reported an error                    */
+#define DORA_ERR_FLAGS      -7  /* unknown flag bits, reserved != 0, or s not finite    */
+
+/*
+ * Bytes of device workspace `op` needs for `shape`: O(d_out*r + r*r + T*r)
+ * for the norm and the GEMM-fused paths, plus one [T, d_out] buffer for the
+ * DORA_FLAG_SEPARATE_COMPOSE forward and for the backward; never d_out*d_in.
+ * Returns 0 if the shape is invalid (the calls then fail with DORA_ERR_SHAPE).
+ */
+DORA_API size_t dora_workspace_bytes(const dora_shape* shape, int op);
+
+/*
+ * Row norms n_i = || W0_i + s (B A)_i ||, in factored form (Scaling DoRA
+ * abstract: base, cross and Gram terms through O(d_out r + r^2)
+ * intermediates; DoRA reading notes Algorithm 1 step 9, per output row).
+ *   W0, A, B   inputs (layer dtype); A and B may be NULL when r == 0
+ *   norm_out   output, float32 [d_out]
+ *   ws         workspace of at least dora_workspace_bytes(shape, DORA_OP_NORM)
+ */
+DORA_API int dora_norm(const dora_shape* shape, const void* W0, const void* A, const void* B,
+                       float* norm_out, void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * Forward of a DoRA linear layer (DoRA reading notes Algorithm 1 steps 7-11):
+ *   norm_out = n (float32 [d_out], as dora_norm),
+ *   xs_out   = s * (x A^T)                  [T, r], layer dtype; NULL = not kept,
+ *   y        = g * (x W0^T + xs B^T) with g = m / max(n, 1e-8),
+ *              composed as base + ((g - 1) base + g s lora) in float32
+ *              and rounded once (Scaling DoRA abstract).
+ *   x, W0, A, B, m   inputs; y, norm_out required outputs; xs_out optional.
+ * y, norm and xs are what dora_backward consumes.
+ */
+DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0, const void* A,
+                          const void* B, const void* m, void* y, float* norm_out, void* xs_out,
+                          void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * Backward of dora_forward for L with dL/dy = grad_y.  By default the norm is
+ * detached, i.e. held constant (DoRA reading notes Sec. 3.4, the default
+ * implementation there):
+ *   grad_m_i = sum_t grad_y[t,i] y[t,i] / m_i          (eq. (8); needs m_i != 0)
+ *   gz       = g * grad_y                               (eq. (7): dV' = (m/n) dW')
+ *   grad_x   = gz W0 + s (gz B) A
+ *   grad_B   = s gz^T (x A^T)      = gz^T xs
+ *   grad_A   = s (gz B)^T x
+ * W0 receives no gradient (it is frozen).  DORA_FLAG_EXACT_NORM_GRAD is not
+ * implemented in this version and returns DORA_ERR_FLAGS.
+ *   grad_y, x, W0, A, B, m, norm, y   inputs (norm and y as written by
+ *                                     dora_forward for the same layer)
+ *   xs        s * (x A^T) as written by dora_forward, or NULL to recompute it
+ *   grad_x [T, d_in], grad_A [r, d_in], grad_B [d_out, r] (layer dtype) and
+ *   grad_m [d_out] (float32): outputs; each may be NULL to skip it.
+ */
+DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const void* x,
+                           const void* W0, const void* A, const void* B, const void* m,
+                           const float* norm, const void* xs, const void* y,
+                           void* grad_x, void* grad_A, void* grad_B, float* grad_m,
+                           void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Static text for a DORA_* return code. */
+DORA_API const char* dora_strerror(int code);
+
+/*
+ * Per-kernel timing, for measurement.  While enabled, every kernel the
+ * library launches is bracketed by a pair of hipEvents recorded on its launch
+ * stream.  dora_timing_collect waits for the recorded events, writes
+ * {"<kernel label>": [launch count, total milliseconds], ...} as JSON text into
+ * buf (NUL-terminated, truncated to buflen), clears the record and returns the
+ * number of launches it covered, or DORA_ERR_HIP.  Enabling/disabling applies
+ * to calls made afterwards, from any thread.
+ */
+DORA_API int dora_timing_enable(int enable);
+DORA_API int dora_timing_collect(char* buf, size_t buflen);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DORA_H */

@@ -39,6 +39,7 @@ __all__ = [
     "NORM_EPS", "lora_update", "adapted_direction", "row_norms", "magnitude_scale",
     "dora_norm", "dora_forward", "dora_backward", "merged_weight", "norm_terms",
     "dora_norm_rows", "dora_forward_entries", "dora_backward_sampled",
+    "scaled_down_projection",
 ]
 
 NORM_EPS = 1e-8
@@ -121,6 +122,16 @@ def dora_backward(gy, x, W0, A, B, m, s, exact=False):
     dA = float(s) * B.T @ dV
     dx = gy @ (g[:, None] * V)                       # y = x W'^T  =>  dx = gy W'
     return dict(dx=dx, dA=dA, dB=dB, dm=dm)
+
+
+def scaled_down_projection(x, A, s):
+    """s * (x @ A^T): the rank-r activations of the low-rank branch, scaled.
+
+    The forward's output splits as y = g * (x W0^T + s (x A^T) B^T) because
+    V' = W0 + s B A ([DN] Alg. 1 steps 8 and 11); this is the factor
+    s (x A^T) that a fast implementation keeps for the backward.
+    """
+    return float(s) * (_f64(x) @ _f64(A).T)
 
 
 def norm_terms(W0, A, B, s):

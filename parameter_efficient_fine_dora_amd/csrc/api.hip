@@ -1,0 +1,483 @@
+// C ABI of libdora.so: argument validation, workspace layout and the launch
+// sequence of the norm, forward and backward.  Every step runs in the
+// kernels of gemm.hip and rowwise.hip; nothing here touches tensor data.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/dora.h"
+#include "kernels.h"
+
+namespace dora {
+namespace {
+
+// ---- per-kernel timing (opt-in) ----------------------------------------------
+
+std::atomic<int> g_timing{0};
+std::mutex g_mu;
+struct Rec {
+  const char* label;
+  hipEvent_t a, b;
+};
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_pool.empty()) {
+      hipEvent_t e = g_pool.back();
+      g_pool.pop_back();
+      return e;
+    }
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// ---- shapes and workspace -------------------------------------------------------
+
+constexpr int64_t kTokPerDmBlock = 64;   // tokens per compose-backward partial sum
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t esize(int dtype) { return dtype == kBF16 ? 2 : 4; }
+
+bool shape_ok(const dora_shape& s) {
+  const int64_t lim = int64_t(1) << 31;
+  if (s.d_out < 1 || s.d_in < 1 || s.r < 0 || s.tokens < 0) return false;
+  if (s.d_out >= lim || s.d_in >= lim || s.r >= lim || s.tokens >= lim) return false;
+  if (s.d_out % 8 || s.d_in % 8 || s.r % 8) return false;
+  const double cap = 4.0e18;
+  if ((double)s.d_out * s.d_in > cap || (double)s.tokens * s.d_out > cap ||
+      (double)s.tokens * s.d_in > cap || (double)s.r * s.d_in > cap)
+    return false;
+  return true;
+}
+
+// Split-K factor for G = A A^T: enough workgroups to cover the chip, at least
+// two 64-deep K tiles per split.
+int gram_splits(const dora_shape& s) {
+  if (s.r == 0) return 1;
+  const int64_t tiles = cdiv(s.r, 64) * cdiv(s.r, 64);
+  const int64_t ktiles = cdiv(s.d_in, 64);
+  int64_t sp = cdiv(256, tiles);
+  sp = std::min<int64_t>(sp, std::max<int64_t>(1, ktiles / 2));
+  sp = std::min<int64_t>(sp, 64);
+  return (int)std::max<int64_t>(sp, 1);
+}
+
+struct Layout {
+  size_t gpart = 0, ghi = 0, glo = 0, P = 0;     // norm
+  size_t xs = 0, slora = 0;                      // forward
+  size_t gz = 0, ts = 0, dmpart = 0;             // backward
+  size_t total = 0;
+  int splits = 1;
+  int64_t dm_blocks = 0;
+};
+
+Layout layout(const dora_shape& s, int op) {
+  Layout L;
+  const size_t e = esize(s.dtype);
+  const size_t r = (size_t)s.r, T = (size_t)s.tokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  if (op == DORA_OP_NORM || op == DORA_OP_FORWARD) {
+    L.splits = gram_splits(s);
+    L.gpart = take((size_t)L.splits * r * r * 4);
+    L.ghi = take(r * r * (s.dtype == kBF16 ? 2 : 4));
+    L.glo = take(s.dtype == kBF16 ? r * r * 2 : 0);
+    L.P = take((size_t)s.d_out * r * 4);
+  }
+  if (op == DORA_OP_FORWARD) {
+    L.xs = take(T * r * e);
+    if (s.flags & DORA_FLAG_SEPARATE_COMPOSE) L.slora = take(T * (size_t)s.d_out * e);
+  }
+  if (op == DORA_OP_BACKWARD) {
+    L.xs = take(T * r * e);
+    L.gz = take(T * (size_t)s.d_out * e);
+    L.ts = take(T * r * e);
+    L.dm_blocks = cdiv(s.tokens, kTokPerDmBlock);
+    L.dmpart = take((size_t)L.dm_blocks * s.d_out * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(const dora_shape* sh, int op, const void* ws, size_t ws_bytes) {
+  if (!sh) return DORA_ERR_NULL;
+  if (sh->reserved != 0) return DORA_ERR_FLAGS;
+  const uint32_t known = DORA_FLAG_EXACT_NORM_GRAD | DORA_FLAG_SEPARATE_COMPOSE;
+  if (sh->flags & ~known) return DORA_ERR_FLAGS;
+  if (!std::isfinite(sh->s)) return DORA_ERR_FLAGS;
+  if (sh->dtype != DORA_F32 && sh->dtype != DORA_BF16) return DORA_ERR_DTYPE;
+  if (!shape_ok(*sh)) return DORA_ERR_SHAPE;
+  const size_t need = layout(*sh, op).total;
+  if (need > 0 && !ws) return DORA_ERR_NULL;
+  if (ws && !aligned(ws)) return DORA_ERR_ALIGN;
+  if (ws_bytes < need) return DORA_ERR_WORKSPACE;
+  return DORA_OK;
+}
+
+// Checks a tensor pointer: required unless the tensor is empty.
+int check_ptr(const void* p, bool empty) {
+  if (!p) return empty ? DORA_OK : DORA_ERR_NULL;
+  return aligned(p) ? DORA_OK : DORA_ERR_ALIGN;
+}
+
+#define DORA_CHECK(expr)          \
+  do {                            \
+    const int rc_ = (expr);       \
+    if (rc_ != DORA_OK) return rc_; \
+  } while (0)
+
+#define HIP_TRY(expr)                                 \
+  do {                                                \
+    if ((expr) != hipSuccess) return DORA_ERR_HIP;    \
+  } while (0)
+
+uint8_t* at(void* ws, size_t off) { return reinterpret_cast<uint8_t*>(ws) + off; }
+
+// Factored norm: G = A A^T (split-K), (s/2) G -> hi/lo, P = 2s W0 A^T + s^2 B G,
+// n_i = sqrt(||W0_i||^2 + B_i . P_i).
+int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, float* norm,
+             void* ws, const Layout& L, hipStream_t st) {
+  const int dt = s.dtype;
+  float* P = nullptr;
+  if (s.r > 0) {
+    float* gpart = reinterpret_cast<float*>(at(ws, L.gpart));
+    void* ghi = at(ws, L.ghi);
+    void* glo = at(ws, L.glo);
+    P = reinterpret_cast<float*>(at(ws, L.P));
+    GemmProblem g;
+    g.M = g.N = s.r;
+    g.nseg = 1;
+    g.seg[0] = {A, A, s.d_in, s.d_in, s.d_in};
+    g.c = gpart;
+    g.ldc = s.r;
+    g.out_f32 = true;
+    g.split = L.splits;
+    g.split_stride = s.r * s.r;
+    HIP_TRY(gemm(g, dt, st, "gram_AAt"));
+    HIP_TRY(gram_finalize(gpart, L.splits, s.r, s.s, dt, ghi, glo, st));
+
+    GemmProblem p;
+    p.M = s.d_out;
+    p.N = s.r;
+    p.seg[0] = {W0, A, s.d_in, s.d_in, s.d_in};
+    p.seg[1] = {B, ghi, s.r, s.r, s.r};
+    p.nseg = 2;
+    if (dt == kBF16) {
+      p.seg[2] = {B, glo, s.r, s.r, s.r};
+      p.nseg = 3;
+    }
+    p.alpha = 2.f * s.s;
+    p.c = P;
+    p.ldc = s.r;
+    p.out_f32 = true;
+    HIP_TRY(gemm(p, dt, st, "cross_gram_proj"));
+  }
+  HIP_TRY(row_norm(W0, B, P, norm, s.d_out, s.d_in, s.r, dt, st));
+  return DORA_OK;
+}
+
+}  // namespace
+
+LaunchTimer::LaunchTimer(const char* label, hipStream_t st) : label_(label), st_(st) {
+  ev_[0] = ev_[1] = nullptr;
+  if (!g_timing.load(std::memory_order_relaxed)) return;
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return;
+  if (hipEventRecord(a, st) != hipSuccess) return;
+  ev_[0] = a;
+  ev_[1] = b;
+}
+
+LaunchTimer::~LaunchTimer() {
+  if (!ev_[0]) return;
+  hipEvent_t a = (hipEvent_t)ev_[0], b = (hipEvent_t)ev_[1];
+  if (hipEventRecord(b, st_) != hipSuccess) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_recs.push_back({label_, a, b});
+}
+
+}  // namespace dora
+
+using namespace dora;
+
+extern "C" {
+
+DORA_API size_t dora_workspace_bytes(const dora_shape* shape, int op) {
+  if (!shape || (shape->dtype != DORA_F32 && shape->dtype != DORA_BF16) || !shape_ok(*shape))
+    return 0;
+  if (op < DORA_OP_NORM || op > DORA_OP_BACKWARD) return 0;
+  return layout(*shape, op).total;
+}
+
+DORA_API int dora_norm(const dora_shape* shape, const void* W0, const void* A, const void* B,
+                       float* norm_out, void* ws, size_t ws_bytes, void* hip_stream) {
+  DORA_CHECK(check_common(shape, DORA_OP_NORM, ws, ws_bytes));
+  const dora_shape& s = *shape;
+  DORA_CHECK(check_ptr(W0, false));
+  DORA_CHECK(check_ptr(A, s.r == 0));
+  DORA_CHECK(check_ptr(B, s.r == 0));
+  DORA_CHECK(check_ptr(norm_out, false));
+  const Layout L = layout(s, DORA_OP_NORM);
+  return run_norm(s, W0, A, B, norm_out, ws, L, reinterpret_cast<hipStream_t>(hip_stream));
+}
+
+DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0, const void* A,
+                          const void* B, const void* m, void* y, float* norm_out, void* xs_out,
+                          void* ws, size_t ws_bytes, void* hip_stream) {
+  DORA_CHECK(check_common(shape, DORA_OP_FORWARD, ws, ws_bytes));
+  const dora_shape& s = *shape;
+  const bool noT = s.tokens == 0;
+  DORA_CHECK(check_ptr(x, noT));
+  DORA_CHECK(check_ptr(W0, false));
+  DORA_CHECK(check_ptr(A, s.r == 0));
+  DORA_CHECK(check_ptr(B, s.r == 0));
+  DORA_CHECK(check_ptr(m, false));
+  DORA_CHECK(check_ptr(y, noT));
+  DORA_CHECK(check_ptr(norm_out, false));
+  DORA_CHECK(check_ptr(xs_out, true));
+  const Layout L = layout(s, DORA_OP_FORWARD);
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  const int dt = s.dtype;
+
+  DORA_CHECK(run_norm(s, W0, A, B, norm_out, ws, L, st));
+  if (noT) return DORA_OK;
+
+  // xs = s (x A^T): the down-projection, pre-scaled by s.
+  void* xs = xs_out ? xs_out : at(ws, L.xs);
+  if (s.r > 0) {
+    GemmProblem d;
+    d.M = s.tokens;
+    d.N = s.r;
+    d.nseg = 1;
+    d.seg[0] = {x, A, s.d_in, s.d_in, s.d_in};
+    d.alpha = s.s;
+    d.c = xs;
+    d.ldc = s.r;
+    HIP_TRY(gemm(d, dt, st, "down_proj_xs"));
+  }
+
+  if (s.flags & DORA_FLAG_SEPARATE_COMPOSE) {
+    // base = x W0^T into y; slora = xs B^T; then the one-pass compose.
+    GemmProblem b;
+    b.M = s.tokens;
+    b.N = s.d_out;
+    b.nseg = 1;
+    b.seg[0] = {x, W0, s.d_in, s.d_in, s.d_in};
+    b.c = y;
+    b.ldc = s.d_out;
+    HIP_TRY(gemm(b, dt, st, "base_gemm"));
+    void* slora = at(ws, L.slora);
+    GemmProblem u;
+    u.M = s.tokens;
+    u.N = s.d_out;
+    u.nseg = 1;
+    u.seg[0] = {xs, B, s.r, s.r, s.r};
+    u.c = slora;
+    u.ldc = s.d_out;
+    HIP_TRY(gemm(u, dt, st, "up_proj_lora"));
+    HIP_TRY(compose_fwd(y, slora, m, norm_out, s.tokens, s.d_out, dt, st));
+    return DORA_OK;
+  }
+
+  // Fused: z = [x | xs] [W0 | B]^T accumulated in one pass, y = z + (g-1) z.
+  GemmProblem f;
+  f.M = s.tokens;
+  f.N = s.d_out;
+  f.seg[0] = {x, W0, s.d_in, s.d_in, s.d_in};
+  f.seg[1] = {xs, B, s.r, s.r, s.r};
+  f.nseg = 2;
+  f.c = y;
+  f.ldc = s.d_out;
+  f.epi = kEpiCompose;
+  f.mag = m;
+  f.norm = norm_out;
+  HIP_TRY(gemm(f, dt, st, "fused_fwd_gemm"));
+  return DORA_OK;
+}
+
+DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const void* x,
+                           const void* W0, const void* A, const void* B, const void* m,
+                           const float* norm, const void* xs, const void* y, void* grad_x,
+                           void* grad_A, void* grad_B, float* grad_m, void* ws, size_t ws_bytes,
+                           void* hip_stream) {
+  DORA_CHECK(check_common(shape, DORA_OP_BACKWARD, ws, ws_bytes));
+  const dora_shape& s = *shape;
+  if (s.flags & DORA_FLAG_EXACT_NORM_GRAD) return DORA_ERR_FLAGS;
+  const bool noT = s.tokens == 0;
+  DORA_CHECK(check_ptr(grad_y, noT));
+  DORA_CHECK(check_ptr(x, noT));
+  DORA_CHECK(check_ptr(W0, false));
+  DORA_CHECK(check_ptr(A, s.r == 0));
+  DORA_CHECK(check_ptr(B, s.r == 0));
+  DORA_CHECK(check_ptr(m, false));
+  DORA_CHECK(check_ptr(norm, false));
+  DORA_CHECK(check_ptr(xs, true));
+  DORA_CHECK(check_ptr(y, noT));
+  DORA_CHECK(check_ptr(grad_x, true));
+  DORA_CHECK(check_ptr(grad_A, true));
+  DORA_CHECK(check_ptr(grad_B, true));
+  DORA_CHECK(check_ptr(grad_m, true));
+  const Layout L = layout(s, DORA_OP_BACKWARD);
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  const int dt = s.dtype;
+  const bool has_r = s.r > 0;
+
+  // gz = g * gy and the dm partial sums.
+  void* gz = at(ws, L.gz);
+  float* dmpart = reinterpret_cast<float*>(at(ws, L.dmpart));
+  const bool need_gz = (grad_x && !noT) || (has_r && (grad_A || grad_B));
+  if (need_gz || grad_m)
+    HIP_TRY(compose_bwd(grad_y, y, m, norm, gz, dmpart, s.tokens, s.d_out, kTokPerDmBlock, dt, st));
+  if (grad_m) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, grad_m, s.d_out, dt, st));
+
+  // ts = s (gz B), needed by grad_x and grad_A.
+  void* ts = at(ws, L.ts);
+  if (has_r && !noT && (grad_x || grad_A)) {
+    GemmProblem t;
+    t.M = s.tokens;
+    t.N = s.r;
+    t.nseg = 1;
+    t.seg[0] = {gz, B, s.d_out, s.r, s.d_out};
+    t.b_kcontig = false;
+    t.alpha = s.s;
+    t.c = ts;
+    t.ldc = s.r;
+    HIP_TRY(gemm(t, dt, st, "t_proj"));
+  }
+
+  if (grad_x && !noT) {
+    GemmProblem d;
+    d.M = s.tokens;
+    d.N = s.d_in;
+    d.seg[0] = {gz, W0, s.d_out, s.d_in, s.d_out};
+    d.seg[1] = {ts, A, s.r, s.d_in, s.r};
+    d.nseg = has_r ? 2 : 1;
+    d.b_kcontig = false;
+    d.c = grad_x;
+    d.ldc = s.d_in;
+    HIP_TRY(gemm(d, dt, st, "dx_gemm"));
+  }
+
+  if (grad_B && has_r) {
+    const void* xsu = xs;
+    if (!xsu && !noT) {
+      void* xw = at(ws, L.xs);
+      GemmProblem d;
+      d.M = s.tokens;
+      d.N = s.r;
+      d.nseg = 1;
+      d.seg[0] = {x, A, s.d_in, s.d_in, s.d_in};
+      d.alpha = s.s;
+      d.c = xw;
+      d.ldc = s.r;
+      HIP_TRY(gemm(d, dt, st, "down_proj_xs"));
+      xsu = xw;
+    }
+    GemmProblem b;
+    b.M = s.d_out;
+    b.N = s.r;
+    b.nseg = 1;
+    b.seg[0] = {gz, xsu, s.d_out, s.r, s.tokens};
+    b.a_kcontig = false;
+    b.b_kcontig = false;
+    b.c = grad_B;
+    b.ldc = s.r;
+    HIP_TRY(gemm(b, dt, st, "dB_gemm"));
+  }
+
+  if (grad_A && has_r) {
+    GemmProblem a;
+    a.M = s.r;
+    a.N = s.d_in;
+    a.nseg = 1;
+    a.seg[0] = {ts, x, s.r, s.d_in, s.tokens};
+    a.a_kcontig = false;
+    a.b_kcontig = false;
+    a.c = grad_A;
+    a.ldc = s.d_in;
+    HIP_TRY(gemm(a, dt, st, "dA_gemm"));
+  }
+  return DORA_OK;
+}
+
+DORA_API const char* dora_strerror(int code) {
+  switch (code) {
+    case DORA_OK: return "ok";
+    case DORA_ERR_NULL: return "a required pointer is NULL";
+    case DORA_ERR_SHAPE: return "invalid shape (dims out of range or not multiples of 8)";
+    case DORA_ERR_DTYPE: return "unsupported dtype";
+    case DORA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case DORA_ERR_WORKSPACE: return "workspace too small";
+    case DORA_ERR_HIP: return "HIP runtime error";
+    case DORA_ERR_FLAGS: return "unsupported flags, nonzero reserved field or non-finite s";
+    default: return "unknown error code";
+  }
+}
+
+DORA_API int dora_timing_enable(int enable) {
+  g_timing.store(enable ? 1 : 0);
+  return DORA_OK;
+}
+
+DORA_API int dora_timing_collect(char* buf, size_t buflen) {
+  std::vector<Rec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    recs.swap(g_recs);
+  }
+  std::map<std::string, std::pair<long, double>> agg;
+  int rc = 0;
+  for (const Rec& r : recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      rc = DORA_ERR_HIP;
+    auto& e = agg[r.label];
+    e.first += 1;
+    e.second += ms;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (const Rec& r : recs) {
+      g_pool.push_back(r.a);
+      g_pool.push_back(r.b);
+    }
+  }
+  std::string out = "{";
+  bool first = true;
+  for (const auto& kv : agg) {
+    char tmp[256];
+    std::snprintf(tmp, sizeof tmp, "%s\"%s\": [%ld, %.6f]", first ? "" : ", ", kv.first.c_str(),
+                  kv.second.first, kv.second.second);
+    out += tmp;
+    first = false;
+  }
+  out += "}";
+  if (buf && buflen) {
+    std::strncpy(buf, out.c_str(), buflen - 1);
+    buf[buflen - 1] = '\0';
+  }
+  return rc ? rc : (int)recs.size();
+}
+
+}  // extern "C"

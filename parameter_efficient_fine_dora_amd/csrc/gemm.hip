@@ -1,0 +1,485 @@
+// Dense contractions of the DoRA hot path on gfx950.
+//
+// bf16 operands run on the CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16,
+// float32 accumulation); float32 layers use a VALU tile kernel.  One kernel
+// template covers every contraction of the path:
+//   C[m, n] = alpha * sum over segments s, k < K_s of opA_s(m, k) * opB_s(n, k)
+// where each operand is either K-contiguous or M/N-contiguous in memory, and
+// up to three K segments are concatenated (e.g. [x | xs] . [W0 | B]^T).
+//
+// Tiling.  A workgroup owns a BM x BN output tile and walks K in 64-deep
+// steps through a double-buffered LDS stage.  LDS rows are 64 bf16 = 128 B,
+// split in eight 16-byte chunks whose order is XOR-swizzled by the row index
+// ((row & 7) ^ ((row >> 3) & 7)) so that the eight rows a 16-byte-per-lane
+// read or write touches land in distinct bank groups.  K-contiguous operands
+// are copied global -> registers -> LDS with 16-byte loads; M/N-contiguous
+// operands are loaded as 4(k) x 8(m) bf16 blocks and transposed in registers
+// before the store, so the MFMA fragment reads are the same for both.
+// Each wave computes a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  The
+// MFMA runs as D = opB-tile x opA-tile^T so that every lane ends up holding
+// four consecutive output columns (8-byte bf16 / 16-byte f32 stores).
+//
+// Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
+// remapped so that consecutive tiles (which share operand panels) run on
+// one XCD and share its L2, and tiles are walked in groups of 4 tile-rows.
+#include "kernels.h"
+#include "common.h"
+
+namespace dora {
+namespace {
+
+constexpr int kBK = 64;           // K depth of one LDS stage (bf16)
+constexpr int kRowBytes = kBK * 2;
+
+struct KArgs {
+  int M, N;
+  int nseg;
+  const uint16_t* a[3];
+  const uint16_t* b[3];
+  int64_t lda[3], ldb[3];
+  int K[3];
+  int kt_end[3];         // cumulative number of K tiles after each segment
+  int kt_per_split;
+  int tiles_m, tiles_n;
+  void* c;
+  int64_t ldc;
+  int64_t split_stride;
+  float alpha;
+  const void* mag;
+  const float* norm;
+};
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
+
+// ---- global -> LDS copies ---------------------------------------------------
+
+// K-contiguous operand: R rows x 64 k, one 16-byte chunk (8 k) per copy.
+template <int R, int NT>
+struct LoadKC {
+  static constexpr int kChunks = R * 8;
+  static constexpr int kPer = (kChunks + NT - 1) / NT;
+  u32x4 v[kPer];
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t ld, int row0, int nrows,
+                                       int k0, int K, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * NT;
+      const int row = c >> 3, kc = c & 7;
+      const int gr = row0 + row, gk = k0 + kc * 8;
+      if ((kChunks % NT == 0 || c < kChunks) && gr < nrows && gk < K)
+        v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)gr * ld + gk);
+      else
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * NT;
+      if (kChunks % NT != 0 && c >= kChunks) continue;
+      const int row = c >> 3, kc = c & 7;
+      *reinterpret_cast<u32x4*>(lds + row * kRowBytes + ((kc ^ swz(row)) << 4)) = v[i];
+    }
+  }
+};
+
+// M/N-contiguous operand: element (row, k) at base[k*ld + row].  Copied as
+// blocks of 4 consecutive k x 8 consecutive rows (four 16-byte loads),
+// transposed in registers into eight 8-byte row pieces.
+template <int R, int NT>
+struct LoadMC {
+  static constexpr int kRowChunks = R / 8;
+  static constexpr int kBlocks = kRowChunks * (kBK / 4);
+  static constexpr int kPer = (kBlocks + NT - 1) / NT;
+  u32x4 v[kPer][4];
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t ld, int row0, int nrows,
+                                       int k0, int K, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int b = tid + i * NT;
+      const int kq = b / kRowChunks, rc = b - kq * kRowChunks;
+      const int gr = row0 + rc * 8;
+      const bool ok = (kBlocks % NT == 0 || b < kBlocks) && gr < nrows;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int gk = k0 + kq * 4 + j;
+        if (ok && gk < K)
+          v[i][j] = *reinterpret_cast<const u32x4*>(base + (int64_t)gk * ld + gr);
+        else
+          v[i][j] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int b = tid + i * NT;
+      if (kBlocks % NT != 0 && b >= kBlocks) continue;
+      const int kq = b / kRowChunks, rc = b - kq * kRowChunks;
+      const int chunk = kq >> 1, half = kq & 1;
+#pragma unroll
+      for (int mm = 0; mm < 8; ++mm) {
+        const int d = mm >> 1;
+        const uint32_t a0 = v[i][0][d], a1 = v[i][1][d], a2 = v[i][2][d], a3 = v[i][3][d];
+        uint32_t lo, hi;
+        if (mm & 1) {
+          lo = (a0 >> 16) | (a1 & 0xffff0000u);
+          hi = (a2 >> 16) | (a3 & 0xffff0000u);
+        } else {
+          lo = (a0 & 0xffffu) | (a1 << 16);
+          hi = (a2 & 0xffffu) | (a3 << 16);
+        }
+        const int row = rc * 8 + mm;
+        *reinterpret_cast<u32x2*>(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4) + half * 8) =
+            u32x2{lo, hi};
+      }
+    }
+  }
+};
+
+template <int R, int NT, bool KC>
+struct Loader;
+template <int R, int NT>
+struct Loader<R, NT, true> : LoadKC<R, NT> {};
+template <int R, int NT>
+struct Loader<R, NT, false> : LoadMC<R, NT> {};
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint8_t* lds, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4));
+}
+
+// Tile index -> (tile_m, tile_n), XCD-grouped, 4 tile-rows per group.
+__device__ __forceinline__ void tile_coords(const KArgs& p, int& tm, int& tn) {
+  int L = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) L = (L & 7) * (nwg >> 3) + (L >> 3);
+  constexpr int kGroup = 4;
+  const int per_group = kGroup * p.tiles_n;
+  const int g = L / per_group;
+  const int first = g * kGroup;
+  const int gsz = min(p.tiles_m - first, kGroup);
+  const int rem = L - g * per_group;
+  tm = first + rem % gsz;
+  tn = rem / gsz;
+}
+
+template <bool OUT_F32>
+__device__ __forceinline__ void store4(const KArgs& p, void* cbase, int m, int n, float v0,
+                                       float v1, float v2, float v3) {
+  if (OUT_F32) {
+    float* c = reinterpret_cast<float*>(cbase) + (int64_t)m * p.ldc + n;
+    *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
+  } else {
+    uint16_t* c = reinterpret_cast<uint16_t*>(cbase) + (int64_t)m * p.ldc + n;
+    *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+  }
+}
+
+// g - 1 for output columns n..n+3 (compose epilogue).
+template <bool BF>
+__device__ __forceinline__ f32x4 gm1_4(const KArgs& p, int n) {
+  f32x4 r;
+  const float* nr = p.norm + n;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float mv = BF ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.mag)[n + e])
+                        : reinterpret_cast<const float*>(p.mag)[n + e];
+    const float nv = fmaxf(nr[e], kNormEps);
+    r[e] = (mv - nv) / nv;
+  }
+  return r;
+}
+
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32>
+__global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int MB = TM / 32, NB = TN / 32;
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes, STAGE = ABYTES + BBYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kt_total = p.kt_end[p.nseg - 1];
+  const int kt_lo = blockIdx.y * p.kt_per_split;
+  const int kt_hi = min(kt_lo + p.kt_per_split, kt_total);
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  Loader<BM, NT, AKC> la;
+  Loader<BN, NT, BKC> lb;
+  auto fetch = [&](int kt) {
+    const int s = kt < p.kt_end[0] ? 0 : (kt < p.kt_end[1] ? 1 : 2);
+    const int k0 = (kt - (s ? p.kt_end[s - 1] : 0)) * kBK;
+    la.load(p.a[s], p.lda[s], m0, p.M, k0, p.K[s], tid);
+    lb.load(p.b[s], p.ldb[s], n0, p.N, k0, p.K[s], tid);
+  };
+
+  if (kt_lo < kt_hi) {
+    fetch(kt_lo);
+    la.store(smem, tid);
+    lb.store(smem + ABYTES, tid);
+    __syncthreads();
+    for (int kt = kt_lo; kt < kt_hi; ++kt) {
+      const int cur = (kt - kt_lo) & 1;
+      const bool more = kt + 1 < kt_hi;
+      if (more) fetch(kt + 1);
+      const uint8_t* As = smem + cur * STAGE;
+      const uint8_t* Bs = As + ABYTES;
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int ch = kk * 2 + (lane >> 5);
+        bf16x8 af[MB], bfg[NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) af[i] = lds_frag(As, wm * TM + i * 32 + (lane & 31), ch);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bfg[j] = lds_frag(Bs, wn * TN + j * 32 + (lane & 31), ch);
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
+      }
+      if (more) {
+        uint8_t* nx = smem + (cur ^ 1) * STAGE;
+        la.store(nx, tid);
+        lb.store(nx + ABYTES, tid);
+      }
+      __syncthreads();
+    }
+  }
+
+  // Epilogue.  acc[i][j][v]: m = m0 + wm*TM + i*32 + lane%32,
+  //                          n = n0 + wn*TN + j*32 + (v/4)*8 + (lane/32)*4 + v%4.
+  void* cbase = OUT_F32 ? (void*)(reinterpret_cast<float*>(p.c) + blockIdx.y * p.split_stride)
+                        : (void*)(reinterpret_cast<uint16_t*>(p.c) + blockIdx.y * p.split_stride);
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = n0 + wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
+      if (n >= p.N) continue;
+      f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
+      if (EPI == kEpiCompose) gm1 = gm1_4<!OUT_F32>(p, n);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int m = m0 + wm * TM + i * 32 + (lane & 31);
+        if (m >= p.M) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float z = p.alpha * acc[i][j][g * 4 + e];
+          v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
+        }
+        store4<OUT_F32>(p, cbase, m, n, v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
+// float32 layers: 64x64 tiles, 16-deep K steps, 4x4 outputs per thread.
+template <bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
+  constexpr int BM = 64, BN = 64, BKF = 16;
+  __shared__ float As[BKF][BM + 4];
+  __shared__ float Bs[BKF][BN + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  float acc[4][4] = {};
+  const int kt_total = p.kt_end[p.nseg - 1];   // in 64-deep units, shared with the bf16 path
+  const int kt_lo = blockIdx.y * p.kt_per_split;
+  const int kt_hi = min(kt_lo + p.kt_per_split, kt_total);
+  for (int kt = kt_lo; kt < kt_hi; ++kt) {
+    const int s = kt < p.kt_end[0] ? 0 : (kt < p.kt_end[1] ? 1 : 2);
+    const int kbase = (kt - (s ? p.kt_end[s - 1] : 0)) * kBK;
+    const float* a = reinterpret_cast<const float*>(p.a[s]);
+    const float* b = reinterpret_cast<const float*>(p.b[s]);
+    for (int ks = 0; ks < kBK; ks += BKF) {
+      const int k0 = kbase + ks;
+      if (k0 >= p.K[s]) break;
+      for (int e = tid; e < BM * BKF; e += 256) {
+        const int mm = AKC ? e / BKF : e % BM, kk = AKC ? e % BKF : e / BM;
+        const int gm = m0 + mm, gk = k0 + kk;
+        float va = 0.f;
+        if (gm < p.M && gk < p.K[s])
+          va = AKC ? a[(int64_t)gm * p.lda[s] + gk] : a[(int64_t)gk * p.lda[s] + gm];
+        As[kk][mm] = va;
+        const int nn = BKC ? e / BKF : e % BN, kb = BKC ? e % BKF : e / BN;
+        const int gn = n0 + nn, gk2 = k0 + kb;
+        float vb = 0.f;
+        if (gn < p.N && gk2 < p.K[s])
+          vb = BKC ? b[(int64_t)gn * p.ldb[s] + gk2] : b[(int64_t)gk2 * p.ldb[s] + gn];
+        Bs[kb][nn] = vb;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < BKF; ++kk) {
+        float ra[4], rb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ra[i] = As[kk][ty * 4 + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rb[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ra[i], rb[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+  }
+  float* c = reinterpret_cast<float*>(p.c) + blockIdx.y * p.split_stride;
+  const int n = n0 + tx * 4;
+  if (n >= p.N) return;
+  f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
+  if (EPI == kEpiCompose) gm1 = gm1_4<false>(p, n);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= p.M) continue;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float z = p.alpha * acc[i][e];
+      v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
+    }
+    store4<true>(p, c, m, n, v[0], v[1], v[2], v[3]);
+  }
+}
+
+// ---- host-side dispatch -----------------------------------------------------
+
+struct TileCfg {
+  int bm, bn;
+};
+
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC>
+hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStream_t st) {
+  const dim3 block(WM * WN * 64);
+  // Only K-contiguous problems (the forward's) use the float32-out and compose epilogues.
+  if constexpr (AKC && BKC) {
+    if (epi == kEpiCompose) {
+      hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiCompose, false>), grid,
+                         block, 0, st, a);
+      return hipGetLastError();
+    }
+    if (out_f32) {
+      hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, true>), grid, block,
+                         0, st, a);
+      return hipGetLastError();
+    }
+  } else {
+    if (epi != kEpiStore || out_f32) return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, false>), grid, block, 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+template <bool AKC, bool BKC>
+hipError_t launch_f32(const KArgs& a, int epi, dim3 grid, hipStream_t st) {
+  if (epi == kEpiCompose)
+    hipLaunchKernelGGL((dora_gemm_f32<AKC, BKC, kEpiCompose>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((dora_gemm_f32<AKC, BKC, kEpiStore>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// Tile size for a bf16 problem: the largest tile that still yields enough
+// workgroups to cover the 256 compute units.
+TileCfg pick_tile(int64_t M, int64_t N) {
+  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (tiles(256, 256) >= 384) return {256, 256};
+  if (tiles(128, 128) >= 160) return {128, 128};
+  return {64, 64};
+}
+
+}  // namespace
+
+int64_t gemm_ktiles(const GemmProblem& p, int /*dtype*/) {
+  int64_t t = 0;
+  for (int s = 0; s < p.nseg; ++s) t += (p.seg[s].K + kBK - 1) / kBK;
+  return t;
+}
+
+hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* label) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  KArgs a{};
+  a.M = (int)p.M;
+  a.N = (int)p.N;
+  // drop empty segments
+  int ns = 0;
+  int kt = 0;
+  for (int s = 0; s < p.nseg; ++s) {
+    if (p.seg[s].K <= 0) continue;
+    a.a[ns] = reinterpret_cast<const uint16_t*>(p.seg[s].a);
+    a.b[ns] = reinterpret_cast<const uint16_t*>(p.seg[s].b);
+    a.lda[ns] = p.seg[s].lda;
+    a.ldb[ns] = p.seg[s].ldb;
+    a.K[ns] = (int)p.seg[s].K;
+    kt += (int)((p.seg[s].K + kBK - 1) / kBK);
+    a.kt_end[ns] = kt;
+    ++ns;
+  }
+  if (ns == 0) {  // empty K: C = 0 (one zero-length segment keeps the kernel uniform)
+    a.a[0] = nullptr;
+    a.b[0] = nullptr;
+    a.K[0] = 0;
+    a.kt_end[0] = 0;
+    ns = 1;
+  }
+  for (int s = ns; s < 3; ++s) a.kt_end[s] = kt;
+  a.nseg = ns;
+  const int split = p.split < 1 ? 1 : p.split;
+  a.kt_per_split = (kt + split - 1) / split;
+  if (a.kt_per_split < 1) a.kt_per_split = 1;
+  a.c = p.c;
+  a.ldc = p.ldc;
+  a.split_stride = p.split_stride;
+  a.alpha = p.alpha;
+  a.mag = p.mag;
+  a.norm = p.norm;
+
+  LaunchTimer timer(label, st);
+  if (dtype == kF32) {
+    a.tiles_m = (int)((p.M + 63) / 64);
+    a.tiles_n = (int)((p.N + 63) / 64);
+    const dim3 grid(a.tiles_m * a.tiles_n, split);
+    if (p.a_kcontig && p.b_kcontig) return launch_f32<true, true>(a, p.epi, grid, st);
+    if (p.a_kcontig) return launch_f32<true, false>(a, p.epi, grid, st);
+    if (p.b_kcontig) return launch_f32<false, true>(a, p.epi, grid, st);
+    return launch_f32<false, false>(a, p.epi, grid, st);
+  }
+
+  const TileCfg t = pick_tile(p.M, p.N);
+  a.tiles_m = (int)((p.M + t.bm - 1) / t.bm);
+  a.tiles_n = (int)((p.N + t.bn - 1) / t.bn);
+  const dim3 grid(a.tiles_m * a.tiles_n, split);
+#define DORA_GEMM_LAYOUTS(BM, BN, WM, WN)                                                 \
+  do {                                                                                    \
+    if (p.a_kcontig && p.b_kcontig)                                                       \
+      return launch_bf16<BM, BN, WM, WN, true, true>(a, p.epi, p.out_f32, grid, st);      \
+    if (p.a_kcontig && !p.b_kcontig)                                                      \
+      return launch_bf16<BM, BN, WM, WN, true, false>(a, p.epi, p.out_f32, grid, st);     \
+    if (!p.a_kcontig && !p.b_kcontig)                                                     \
+      return launch_bf16<BM, BN, WM, WN, false, false>(a, p.epi, p.out_f32, grid, st);    \
+    return hipErrorInvalidValue;                                                          \
+  } while (0)
+  if (t.bm == 256) DORA_GEMM_LAYOUTS(256, 256, 2, 4);
+  if (t.bm == 128) DORA_GEMM_LAYOUTS(128, 128, 2, 2);
+  DORA_GEMM_LAYOUTS(64, 64, 2, 2);
+#undef DORA_GEMM_LAYOUTS
+}
+
+}  // namespace dora

@@ -1,0 +1,77 @@
+// Internal interface between the C ABI (api.hip) and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dora {
+
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+// One K segment of C += op(A) op(B)^T.  Element (m, k) of op(A) is
+// a[m*lda + k] when the A operand is K-contiguous, a[k*lda + m] otherwise;
+// element (n, k) of op(B) likewise with b / ldb.
+struct GemmSeg {
+  const void* a;
+  const void* b;
+  int64_t lda, ldb;
+  int64_t K;
+};
+
+enum Epilogue : int {
+  kEpiStore = 0,     // C = alpha * acc
+  kEpiCompose = 1,   // C = z + (g - 1) z with z = alpha * acc, g_n = m_n / max(norm_n, eps)
+};
+
+struct GemmProblem {
+  int64_t M = 0, N = 0;
+  int nseg = 0;
+  GemmSeg seg[3] = {};
+  bool a_kcontig = true, b_kcontig = true;   // same for every segment
+  void* c = nullptr;
+  int64_t ldc = 0;
+  float alpha = 1.f;
+  bool out_f32 = false;        // C is float32 (else the layer dtype)
+  int split = 1;               // split-K factor: C_z written at c + z*split_stride
+  int64_t split_stride = 0;    // elements
+  int epi = kEpiStore;
+  const void* mag = nullptr;   // kEpiCompose: m [N] (layer dtype)
+  const float* norm = nullptr; // kEpiCompose: n [N] float32
+};
+
+// Enqueue C = sum over segments; picks the tile configuration from the shape.
+hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* label);
+
+// Number of 64-deep K tiles a segment list spans (used for split-K sizing).
+int64_t gemm_ktiles(const GemmProblem& p, int dtype);
+
+// G partial sums -> (s/2) * G, symmetrised; bf16: written as hi + lo bf16 pair.
+hipError_t gram_finalize(const float* part, int splits, int64_t r, float s, int dtype,
+                         void* g_hi, void* g_lo, hipStream_t st);
+
+// n_i = sqrt(max(0, ||W0_i||^2 + B_i . P_i)).
+hipError_t row_norm(const void* W0, const void* B, const float* P, float* norm, int64_t d_out,
+                    int64_t d_in, int64_t r, int dtype, hipStream_t st);
+
+// y = base + ((g-1) base + g * slora) in place on y (base), slora = s * lora.
+hipError_t compose_fwd(void* y, const void* slora, const void* m, const float* norm, int64_t T,
+                       int64_t d_out, int dtype, hipStream_t st);
+
+// gz = g * gy; dm_part[b, i] = sum over token block b of gy * y.
+hipError_t compose_bwd(const void* gy, const void* y, const void* m, const float* norm, void* gz,
+                       float* dm_part, int64_t T, int64_t d_out, int64_t tokens_per_block,
+                       int dtype, hipStream_t st);
+
+// dm_i = sum_b dm_part[b, i] / m_i (fixed order).
+hipError_t dm_finalize(const float* dm_part, int64_t blocks, const void* m, float* dm,
+                       int64_t d_out, int dtype, hipStream_t st);
+
+// Launch bookkeeping for the optional per-kernel timing.
+struct LaunchTimer {
+  LaunchTimer(const char* label, hipStream_t st);
+  ~LaunchTimer();
+  const char* label_;
+  hipStream_t st_;
+  void* ev_[2];
+};
+
+}  // namespace dora

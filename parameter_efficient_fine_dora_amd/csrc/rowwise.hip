@@ -1,0 +1,296 @@
+// Bandwidth-bound kernels of the DoRA hot path on gfx950: the Gram finisher,
+// the factored row norm, and the standalone compose forward / backward.
+// Every tensor is streamed with 16-byte vector loads along its contiguous
+// dimension (8 bf16 or 4 float32 per load), accumulation is float32.
+#include "kernels.h"
+#include "common.h"
+
+namespace dora {
+namespace {
+
+template <bool BF>
+struct Vec;   // one 16-byte vector of the layer dtype
+template <>
+struct Vec<true> {
+  static constexpr int kN = 8;
+  __device__ static void load(const void* p, int64_t i, float* out) {   // i in vectors
+    const u32x4 v = reinterpret_cast<const u32x4*>(p)[i];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      out[2 * d] = bf_lo(v[d]);
+      out[2 * d + 1] = bf_hi(v[d]);
+    }
+  }
+  __device__ static void store(void* p, int64_t i, const float* in) {
+    u32x4 v;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) v[d] = pack_bf16x2(in[2 * d], in[2 * d + 1]);
+    reinterpret_cast<u32x4*>(p)[i] = v;
+  }
+  __device__ static float scalar(const void* p, int64_t i) {
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  }
+};
+template <>
+struct Vec<false> {
+  static constexpr int kN = 4;
+  __device__ static void load(const void* p, int64_t i, float* out) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(p)[i];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) out[d] = v[d];
+  }
+  __device__ static void store(void* p, int64_t i, const float* in) {
+    reinterpret_cast<f32x4*>(p)[i] = f32x4{in[0], in[1], in[2], in[3]};
+  }
+  __device__ static float scalar(const void* p, int64_t i) {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---- Gram finisher ------------------------------------------------------------
+// part[z][j][l], z < splits: split-K partial sums of G = A A^T.  Writes
+// (s/2) * G, symmetrised as (G[j][l] + G[l][j]) / 2 so that B (s/2 G)^T is
+// exactly B (s/2 G).  bf16 layers get it as a hi + lo bf16 pair (hi = round(v),
+// lo = round(v - hi)), which keeps ~16 significant bits through the bf16 MFMA.
+__global__ __launch_bounds__(256) void dora_gram_finalize(const float* part, int splits,
+                                                          int64_t r, float quarter_s, int bf,
+                                                          void* g_hi, void* g_lo) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= r * r) return;
+  const int64_t j = idx / r, l = idx - j * r;
+  const int64_t rr = r * r;
+  float a = 0.f, b = 0.f;
+  for (int z = 0; z < splits; ++z) {
+    a += part[z * rr + j * r + l];
+    b += part[z * rr + l * r + j];
+  }
+  const float v = quarter_s * (a + b);
+  if (bf) {
+    const uint16_t hi = f32_to_bf16(v);
+    const float rest = v - bf16_to_f32(hi);
+    reinterpret_cast<uint16_t*>(g_hi)[idx] = hi;
+    reinterpret_cast<uint16_t*>(g_lo)[idx] = f32_to_bf16(rest);
+  } else {
+    reinterpret_cast<float*>(g_hi)[idx] = v;
+  }
+}
+
+// ---- factored row norm --------------------------------------------------------
+// One wave per output row i:
+//   n_i^2 = sum_k W0_ik^2 + sum_j B_ij P_ij,   P = 2s W0 A^T + s^2 B G,
+// i.e. base + cross + Gram.  W0's row is streamed once with 16-byte loads,
+// four in flight per lane; B_i and P_i are read once each (no reuse, so they
+// go straight to registers) and the lane partials meet in a wave reduction.
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_row_norm(const void* W0, const void* B, const float* P,
+                                                     float* norm, int64_t d_out, int64_t d_in,
+                                                     int64_t r) {
+  using V = Vec<BF>;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= d_out) return;   // whole wave leaves; the kernel has no barrier
+  const int64_t nv = d_in / V::kN;
+  const int64_t wbase = row * nv;
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  int64_t c = lane;
+  for (; c + 192 < nv; c += 256) {
+    float a[V::kN], b[V::kN], e[V::kN], f[V::kN];
+    V::load(W0, wbase + c, a);
+    V::load(W0, wbase + c + 64, b);
+    V::load(W0, wbase + c + 128, e);
+    V::load(W0, wbase + c + 192, f);
+#pragma unroll
+    for (int q = 0; q < V::kN; ++q) {
+      acc0 = fmaf(a[q], a[q], acc0);
+      acc1 = fmaf(b[q], b[q], acc1);
+      acc2 = fmaf(e[q], e[q], acc2);
+      acc3 = fmaf(f[q], f[q], acc3);
+    }
+  }
+  for (; c < nv; c += 64) {
+    float a[V::kN];
+    V::load(W0, wbase + c, a);
+#pragma unroll
+    for (int q = 0; q < V::kN; ++q) acc0 = fmaf(a[q], a[q], acc0);
+  }
+  // cross + Gram: B_i . P_i
+  const int64_t rv = r / V::kN;
+  const float* prow = P + row * r;
+  for (int64_t cc = lane; cc < rv; cc += 64) {
+    float bv[V::kN];
+    V::load(B, row * rv + cc, bv);
+#pragma unroll
+    for (int q = 0; q < V::kN; q += 4) {
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(prow + cc * V::kN + q);
+      acc1 = fmaf(bv[q], pv[0], acc1);
+      acc1 = fmaf(bv[q + 1], pv[1], acc1);
+      acc1 = fmaf(bv[q + 2], pv[2], acc1);
+      acc1 = fmaf(bv[q + 3], pv[3], acc1);
+    }
+  }
+  const float tot = wave_sum((acc0 + acc1) + (acc2 + acc3));
+  if (lane == 0) norm[row] = sqrtf(fmaxf(tot, 0.f));
+}
+
+// ---- compose forward ------------------------------------------------------------
+// y = base + ((g - 1) base + g * slora), base read from y and overwritten,
+// slora = s (x A^T) B^T, g - 1 = (m - n) / n with n clamped at kNormEps,
+// everything in float32 and rounded once.  Thread = one 16-byte column vector,
+// looping over a block of tokens; g and g - 1 are formed once per thread.
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_compose_fwd(void* y, const void* slora, const void* m,
+                                                        const float* norm, int64_t T,
+                                                        int64_t d_out, int64_t tok_per_block) {
+  using V = Vec<BF>;
+  const int64_t nvec = d_out / V::kN;
+  const int64_t cv = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (cv >= nvec) return;
+  float g[V::kN], gm1[V::kN];
+#pragma unroll
+  for (int q = 0; q < V::kN; ++q) {
+    const int64_t col = cv * V::kN + q;
+    const float n = fmaxf(norm[col], kNormEps);
+    const float mv = V::scalar(m, col);
+    gm1[q] = (mv - n) / n;
+    g[q] = mv / n;
+  }
+  const int64_t t0 = (int64_t)blockIdx.y * tok_per_block;
+  const int64_t t1 = min(T, t0 + tok_per_block);
+  for (int64_t t = t0; t < t1; ++t) {
+    float base[V::kN], lo[V::kN], out[V::kN];
+    V::load(y, t * nvec + cv, base);
+    V::load(slora, t * nvec + cv, lo);
+#pragma unroll
+    for (int q = 0; q < V::kN; ++q) out[q] = base[q] + fmaf(gm1[q], base[q], g[q] * lo[q]);
+    V::store(y, t * nvec + cv, out);
+  }
+}
+
+// ---- compose backward -------------------------------------------------------------
+// With the norm detached (held constant), y = g z gives dL/dz = g * gy and
+// dL/dm_i = sum_t gy[t,i] z[t,i] / n_i = sum_t gy[t,i] y[t,i] / m_i.
+// This kernel writes gz = g * gy and, per token block b, the column partial
+// sums dm_part[b, i] = sum_{t in b} gy[t,i] y[t,i]; dora_dm_finalize adds the
+// blocks in a fixed order, so the result does not depend on scheduling.
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_compose_bwd(const void* gy, const void* y,
+                                                        const void* m, const float* norm, void* gz,
+                                                        float* dm_part, int64_t T, int64_t d_out,
+                                                        int64_t tok_per_block) {
+  using V = Vec<BF>;
+  const int64_t nvec = d_out / V::kN;
+  const int64_t cv = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (cv >= nvec) return;
+  float g[V::kN], acc[V::kN];
+#pragma unroll
+  for (int q = 0; q < V::kN; ++q) {
+    const int64_t col = cv * V::kN + q;
+    g[q] = V::scalar(m, col) / fmaxf(norm[col], kNormEps);
+    acc[q] = 0.f;
+  }
+  const int64_t t0 = (int64_t)blockIdx.y * tok_per_block;
+  const int64_t t1 = min(T, t0 + tok_per_block);
+  for (int64_t t = t0; t < t1; ++t) {
+    float a[V::kN], b[V::kN], o[V::kN];
+    V::load(gy, t * nvec + cv, a);
+    V::load(y, t * nvec + cv, b);
+#pragma unroll
+    for (int q = 0; q < V::kN; ++q) {
+      o[q] = g[q] * a[q];
+      acc[q] = fmaf(a[q], b[q], acc[q]);
+    }
+    V::store(gz, t * nvec + cv, o);
+  }
+  float* dst = dm_part + (int64_t)blockIdx.y * d_out + cv * V::kN;
+#pragma unroll
+  for (int q = 0; q < V::kN; q += 4)
+    *reinterpret_cast<f32x4*>(dst + q) = f32x4{acc[q], acc[q + 1], acc[q + 2], acc[q + 3]};
+}
+
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_dm_finalize(const float* dm_part, int64_t blocks,
+                                                        const void* m, float* dm, int64_t d_out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= d_out) return;
+  float s = 0.f;
+  for (int64_t b = 0; b < blocks; ++b) s += dm_part[b * d_out + i];
+  dm[i] = s / Vec<BF>::scalar(m, i);
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+hipError_t gram_finalize(const float* part, int splits, int64_t r, float s, int dtype, void* g_hi,
+                         void* g_lo, hipStream_t st) {
+  if (r <= 0) return hipSuccess;
+  LaunchTimer t("gram_finalize", st);
+  hipLaunchKernelGGL(dora_gram_finalize, dim3((unsigned)cdiv(r * r, 256)), dim3(256), 0, st, part,
+                     splits, r, 0.25f * s, dtype == kBF16 ? 1 : 0, g_hi, g_lo);
+  return hipGetLastError();
+}
+
+hipError_t row_norm(const void* W0, const void* B, const float* P, float* norm, int64_t d_out,
+                    int64_t d_in, int64_t r, int dtype, hipStream_t st) {
+  LaunchTimer t("row_norm", st);
+  const dim3 grid((unsigned)cdiv(d_out, 4));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dora_row_norm<true>, grid, dim3(256), 0, st, W0, B, P, norm, d_out, d_in, r);
+  else
+    hipLaunchKernelGGL(dora_row_norm<false>, grid, dim3(256), 0, st, W0, B, P, norm, d_out, d_in,
+                       r);
+  return hipGetLastError();
+}
+
+hipError_t compose_fwd(void* y, const void* slora, const void* m, const float* norm, int64_t T,
+                       int64_t d_out, int dtype, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  LaunchTimer t("compose_fwd", st);
+  const int64_t vec = dtype == kBF16 ? 8 : 4;
+  const int64_t tpb = 16;
+  const dim3 grid((unsigned)cdiv(d_out / vec, 256), (unsigned)cdiv(T, tpb));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dora_compose_fwd<true>, grid, dim3(256), 0, st, y, slora, m, norm, T, d_out,
+                       tpb);
+  else
+    hipLaunchKernelGGL(dora_compose_fwd<false>, grid, dim3(256), 0, st, y, slora, m, norm, T,
+                       d_out, tpb);
+  return hipGetLastError();
+}
+
+hipError_t compose_bwd(const void* gy, const void* y, const void* m, const float* norm, void* gz,
+                       float* dm_part, int64_t T, int64_t d_out, int64_t tokens_per_block,
+                       int dtype, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  LaunchTimer t("compose_bwd", st);
+  const int64_t vec = dtype == kBF16 ? 8 : 4;
+  const dim3 grid((unsigned)cdiv(d_out / vec, 256), (unsigned)cdiv(T, tokens_per_block));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dora_compose_bwd<true>, grid, dim3(256), 0, st, gy, y, m, norm, gz, dm_part,
+                       T, d_out, tokens_per_block);
+  else
+    hipLaunchKernelGGL(dora_compose_bwd<false>, grid, dim3(256), 0, st, gy, y, m, norm, gz,
+                       dm_part, T, d_out, tokens_per_block);
+  return hipGetLastError();
+}
+
+hipError_t dm_finalize(const float* dm_part, int64_t blocks, const void* m, float* dm,
+                       int64_t d_out, int dtype, hipStream_t st) {
+  LaunchTimer t("dm_finalize", st);
+  const dim3 grid((unsigned)cdiv(d_out, 256));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dora_dm_finalize<true>, grid, dim3(256), 0, st, dm_part, blocks, m, dm,
+                       d_out);
+  else
+    hipLaunchKernelGGL(dora_dm_finalize<false>, grid, dim3(256), 0, st, dm_part, blocks, m, dm,
+                       d_out);
+  return hipGetLastError();
+}
+
+}  // namespace dora

@@ -1,0 +1,62 @@
+"""DoRA linear layer on top of the C ABI (autograd glue only).
+
+Forward saves norm, xs = s (x A^T) and y for the backward; the norm is
+detached there (DoRA reading notes, Sec. 3.4).
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import ops
+
+
+class DoRAFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, W0, A, B, m, s, flags):
+        y, norm, xs = ops.dora_forward(x, W0, A, B, m, s, flags=flags)
+        ctx.s = s
+        ctx.flags = flags
+        ctx.save_for_backward(x, W0, A, B, m, norm, xs, y)
+        ctx.mark_non_differentiable(norm)
+        return y, norm
+
+    @staticmethod
+    def backward(ctx, gy, _gnorm):
+        x, W0, A, B, m, norm, xs, y = ctx.saved_tensors
+        need = tuple(n for n, k in (("x", 0), ("A", 2), ("B", 3), ("m", 4))
+                     if ctx.needs_input_grad[k])
+        gx, gA, gB, gm = ops.dora_backward(gy.contiguous(), x, W0, A, B, m, norm, xs, y, ctx.s,
+                                           need=need, flags=ctx.flags)
+        if gm is not None:
+            gm = gm.to(m.dtype)
+        return gx, None, gA, gB, gm, None, None
+
+
+class DoRALinear(torch.nn.Module):
+    """y = (m / ||W0 + s B A||_row) * (x W0^T + s (x A^T) B^T), W0 frozen.
+
+    Initialised as DoRA starts training (DoRA reading notes, Algorithm 1
+    steps 1-4): m = row norms of W0, A Kaiming-uniform, B = 0.
+    """
+
+    def __init__(self, weight: torch.Tensor, r: int, s: float = 2.0, flags: int = 0):
+        super().__init__()
+        d_out, d_in = weight.shape
+        dev, dt = weight.device, weight.dtype
+        self.register_buffer("W0", weight.detach().contiguous())
+        self.A = torch.nn.Parameter(torch.empty(r, d_in, device=dev, dtype=dt))
+        torch.nn.init.kaiming_uniform_(self.A, a=math.sqrt(5))
+        self.B = torch.nn.Parameter(torch.zeros(d_out, r, device=dev, dtype=dt))
+        self.m = torch.nn.Parameter(torch.empty(d_out, device=dev, dtype=dt))
+        with torch.no_grad():
+            self.m.copy_(ops.dora_norm(self.W0, self.A, self.B, s).to(dt))
+        self.s = float(s)
+        self.flags = int(flags)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1]).contiguous()
+        y, _ = DoRAFunction.apply(x2, self.W0, self.A, self.B, self.m, self.s, self.flags)
+        return y.reshape(*lead, y.shape[-1])

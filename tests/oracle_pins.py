@@ -97,6 +97,9 @@ def pin_bruteforce(orc):
         y, n = orc.dora_forward(x, W0, A, B, m, s)
         _close(n, n_ref, 1e-13, "brute forward norm")
         _close(y, y_ref, 1e-13, "brute y")
+        xs_ref = [[s * sum(x[t][k] * A[j][k] for k in range(d_in)) for j in range(r)]
+                  for t in range(T)]
+        _close(orc.scaled_down_projection(x, A, s), xs_ref, 1e-13, "brute xs")
 
 
 def pin_factored_identity(orc):

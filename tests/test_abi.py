@@ -1,0 +1,127 @@
+"""The C ABI on the host: libdora.so loads, exports every declared symbol, and
+rejects bad arguments before touching the GPU.  No compute calls here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from parameter_efficient_fine_dora_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dora.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libdora.so not built")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"DORA_API\s+[\w\s\*]+?\b(dora_\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_symbols())
+    assert {"dora_norm", "dora_forward", "dora_backward", "dora_workspace_bytes",
+            "dora_strerror", "dora_timing_enable", "dora_timing_collect"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_shape_struct_matches_header():
+    assert ctypes.sizeof(_lib.DoraShape) == 48
+    assert _lib.DoraShape.s.offset == 36 and _lib.DoraShape.flags.offset == 40
+
+
+def test_strerror_texts():
+    for code in _lib.ERR:
+        assert _lib.strerror(code)
+    assert "unknown" in _lib.strerror(-99)
+
+
+FAKE = 0x10000  # 16-byte aligned host address; validation never dereferences it
+
+
+def _norm(sh, W0=FAKE, A=FAKE, B=FAKE, out=FAKE, ws=FAKE, nb=1 << 40):
+    return _lib.lib().dora_norm(ctypes.byref(sh) if sh is not None else None, W0, A, B, out, ws,
+                                nb, None)
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((0, 64, 8, 4), "DORA_ERR_SHAPE"), ((64, 0, 8, 4), "DORA_ERR_SHAPE"),
+    ((64, 64, -8, 4), "DORA_ERR_SHAPE"), ((64, 64, 8, -1), "DORA_ERR_SHAPE"),
+    ((60, 64, 8, 4), "DORA_ERR_SHAPE"), ((64, 66, 8, 4), "DORA_ERR_SHAPE"),
+    ((64, 64, 12, 4), "DORA_ERR_SHAPE"), ((1 << 31, 8, 8, 4), "DORA_ERR_SHAPE"),
+    ((64, 64, 1 << 31, 8), "DORA_ERR_SHAPE"), ((64, 64, 8, 1 << 31), "DORA_ERR_SHAPE"),
+])
+def test_bad_shapes_rejected(dims, code):
+    sh = _lib.shape(*dims, _lib.BF16, 2.0)
+    assert _norm(sh) == _lib.ERR_CODE[code]
+    assert _lib.workspace_bytes(sh, _lib.OP_NORM) == 0
+
+
+def test_validation_codes():
+    ok = _lib.shape(64, 64, 8, 4, _lib.BF16, 2.0)
+    assert _norm(None) == _lib.ERR_CODE["DORA_ERR_NULL"]
+    assert _norm(_lib.shape(64, 64, 8, 4, 7, 2.0)) == _lib.ERR_CODE["DORA_ERR_DTYPE"]
+    assert _norm(_lib.shape(64, 64, 8, 4, _lib.BF16, float("nan"))) == _lib.ERR_CODE["DORA_ERR_FLAGS"]
+    assert _norm(_lib.shape(64, 64, 8, 4, _lib.BF16, 2.0, 1 << 7)) == _lib.ERR_CODE["DORA_ERR_FLAGS"]
+    bad = _lib.shape(64, 64, 8, 4, _lib.BF16, 2.0)
+    bad.reserved = 1
+    assert _norm(bad) == _lib.ERR_CODE["DORA_ERR_FLAGS"]
+    assert _norm(ok, W0=None) == _lib.ERR_CODE["DORA_ERR_NULL"]
+    assert _norm(ok, A=None) == _lib.ERR_CODE["DORA_ERR_NULL"]
+    assert _norm(ok, out=None) == _lib.ERR_CODE["DORA_ERR_NULL"]
+    assert _norm(ok, ws=None) == _lib.ERR_CODE["DORA_ERR_NULL"]
+    assert _norm(ok, W0=FAKE + 2) == _lib.ERR_CODE["DORA_ERR_ALIGN"]
+    assert _norm(ok, ws=FAKE + 8) == _lib.ERR_CODE["DORA_ERR_ALIGN"]
+    need = _lib.workspace_bytes(ok, _lib.OP_NORM)
+    assert _norm(ok, nb=need - 1) == _lib.ERR_CODE["DORA_ERR_WORKSPACE"]
+    # rank 0: A and B may be NULL, W0 may not (only failing paths are exercised here:
+    # a call that passes validation would enqueue kernels)
+    r0 = _lib.shape(64, 64, 0, 4, _lib.BF16, 2.0)
+    assert _norm(r0, W0=None, A=None, B=None) == _lib.ERR_CODE["DORA_ERR_NULL"]
+
+
+def test_backward_exact_flag_is_rejected_on_host():
+    sh = _lib.shape(64, 64, 8, 4, _lib.BF16, 2.0, _lib.FLAG_EXACT_NORM_GRAD)
+    nb = _lib.workspace_bytes(sh, _lib.OP_BACKWARD)
+    args = [FAKE] * 13
+    rc = _lib.lib().dora_backward(ctypes.byref(sh), *args, FAKE, nb, None)
+    assert rc == _lib.ERR_CODE["DORA_ERR_FLAGS"]
+
+
+def test_workspace_never_scales_with_d_out_times_d_in():
+    """Zero transient d_out x d_in buffers: the workspace is O(d_out r + r^2 + T r) (+ [T, d_out])."""
+    for d_out, d_in, r, T in [(8192, 8192, 384, 4096), (27648, 5120, 256, 8192), (2048, 6144, 64, 2048)]:
+        sh = _lib.shape(d_out, d_in, r, T, _lib.BF16, 2.0)
+        dense = d_out * d_in * 2
+        norm_ws = _lib.workspace_bytes(sh, _lib.OP_NORM)
+        fwd_ws = _lib.workspace_bytes(sh, _lib.OP_FORWARD)
+        bwd_ws = _lib.workspace_bytes(sh, _lib.OP_BACKWARD)
+        assert norm_ws < dense / 4
+        assert norm_ws <= 64 * r * r * 4 + r * r * 4 + d_out * r * 4 + 4096
+        assert fwd_ws - norm_ws <= T * r * 2 + 512
+        assert bwd_ws <= T * d_out * 2 + 2 * T * r * 2 + ((T + 63) // 64) * d_out * 4 + 4096
+        sep = _lib.shape(d_out, d_in, r, T, _lib.BF16, 2.0, _lib.FLAG_SEPARATE_COMPOSE)
+        assert _lib.workspace_bytes(sep, _lib.OP_FORWARD) - fwd_ws >= T * d_out * 2
+
+
+def test_timing_collect_empty_on_host():
+    L = _lib.lib()
+    assert L.dora_timing_enable(0) == 0
+    buf = ctypes.create_string_buffer(64)
+    assert L.dora_timing_collect(buf, 64) == 0
+    assert buf.value == b"{}"
+
+
+def test_library_has_no_device_allocation_calls():
+    """The library allocates nothing: no hipMalloc/hipFree in its sources."""
+    csrc = os.path.join(ROOT, "parameter_efficient_fine_dora_amd", "csrc")
+    for fn in os.listdir(csrc):
+        text = open(os.path.join(csrc, fn)).read()
+        for bad in ("hipMalloc", "hipFree", "hipHostMalloc", "hipExtMalloc"):
+            assert bad not in text, (fn, bad)

@@ -1,0 +1,393 @@
+"""HIP path vs the float64 oracle, element by element, through the C ABI.
+
+Every case draws its inputs from synth (identical bits on both sides), runs
+dora_norm / dora_forward / dora_backward on the GPU through the torch binding
+(marshalling only) and compares with the oracle at the parity bars stated in
+tests/gpu_util.py.  Full-size layers are compared on sampled outputs (and
+on every row norm).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import LayerShape
+from tests.gpu_util import (check_norm, check_out, download, layer_to_device, out_stats, upload)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_rows.json")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ops():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from parameter_efficient_fine_dora_amd import ops as _ops, _lib
+    _lib.lib()  # raises if the library is missing: there is no fallback
+    return _ops
+
+
+def run_layer(ops, shape: LayerShape, layer: dict, flags=0, backward=True, need=("x", "A", "B", "m")):
+    dev = layer_to_device(layer, shape.dtype)
+    y, norm, xs = ops.dora_forward(dev["x"], dev["W0"], dev["A"], dev["B"], dev["m"], shape.s,
+                                   flags=flags)
+    out = dict(y=y, norm=norm, xs=xs)
+    if backward:
+        gx, gA, gB, gm = ops.dora_backward(dev["gy"], dev["x"], dev["W0"], dev["A"], dev["B"],
+                                           dev["m"], norm, xs, y, shape.s, need=need, flags=flags)
+        out.update(dx=gx, dA=gA, dB=gB, dm=gm)
+    torch.cuda.synchronize()
+    return {k: (download(v) if v is not None else None) for k, v in out.items()}
+
+
+def compare_full(shape, layer, got, backward=True):
+    L = synth.layer_f64(layer, shape.dtype)
+    y_ref, n_ref = oracle.dora_forward(L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
+    check_norm(got["norm"], n_ref, "norm")
+    if shape.tokens:
+        check_out(got["y"], y_ref, "y")
+        if shape.r:
+            check_out(got["xs"], oracle.scaled_down_projection(L["x"], L["A"], shape.s), "xs")
+    if backward:
+        g = oracle.dora_backward(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
+        for k in ("dx", "dA", "dB", "dm"):
+            if got.get(k) is not None and g[k].size:
+                check_out(got[k], g[k], k)
+
+
+# ---- hand-worked integer rows: bit-exact ---------------------------------------
+
+def golden_layer(e, dtype):
+    """Embed one worked example in a layer padded to multiples of 8.
+
+    Rows past the example's are unit rows W0_i = e_{d_in-1}, B_i = 0, m_i = 1
+    (n_i = 1), with x and gy zero in the padded columns, so they add nothing to
+    the example's outputs.
+    """
+    W0e, Ae, Be = (np.array(e[k], dtype=np.float64) for k in ("W0", "A", "B"))
+    d_oe, d_ie = W0e.shape
+    r_e = Ae.shape[0]
+    d_out, d_in, r = 8, 8, 8
+    W0 = np.zeros((d_out, d_in)); W0[:d_oe, :d_ie] = W0e
+    for i in range(d_oe, d_out):
+        W0[i, d_in - 1] = 1.0
+    A = np.zeros((r, d_in)); A[:r_e, :d_ie] = Ae
+    B = np.zeros((d_out, r)); B[:d_oe, :r_e] = Be
+    m = np.ones(d_out); m[:d_oe] = e.get("m", np.ones(d_oe))
+    xe = np.array(e.get("x", [[1.0] * d_ie]), dtype=np.float64)
+    T = xe.shape[0]
+    x = np.zeros((T, d_in)); x[:, :d_ie] = xe
+    gy = np.zeros((T, d_out)); gy[:, :d_oe] = np.array(e.get("gy", np.zeros((T, d_oe))))
+    store = (lambda a: synth.bf16_bits(a.astype(np.float32))) if dtype == "bf16" else (
+        lambda a: a.astype(np.float32))
+    layer = {k: store(v) for k, v in dict(W0=W0, A=A, B=B, m=m, x=x, gy=gy).items()}
+    return LayerShape(d_out, d_in, r, T, e["s"], dtype), layer, d_oe, d_ie, r_e
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("flags", [0, 2])
+def test_worked_rows_exact(ops, dtype, flags):
+    for e in json.load(open(GOLDEN))["examples"]:
+        say(f"worked row {e['name']} {dtype} flags={flags}")
+        shape, layer, d_oe, d_ie, r_e = golden_layer(e, dtype)
+        got = run_layer(ops, shape, layer, flags=flags)
+        n = got["norm"][:d_oe]
+        n_exp = np.array(e["norm"], float)
+        if all(float(v).is_integer() for v in n_exp):
+            assert np.array_equal(n, n_exp), (e["name"], n)
+        else:   # n^2 is exact; the float32 square root is correctly rounded
+            np.testing.assert_allclose(n, n_exp, rtol=2e-7, atol=0)
+        if "y" in e:
+            y_exp = np.array(e["y"], float)
+            if all(float(v).is_integer() for v in y_exp.ravel()):
+                assert np.array_equal(got["y"][:, :d_oe], y_exp), got["y"]
+            else:
+                np.testing.assert_allclose(got["y"][:, :d_oe], y_exp, rtol=2 ** -8)
+        if "gy" in e:
+            assert np.array_equal(got["dx"][:, :d_ie], np.array(e["dx"], float)), got["dx"]
+            assert np.array_equal(got["dA"][:r_e, :d_ie], np.array(e["dA"], float)), got["dA"]
+            assert np.array_equal(got["dB"][:d_oe, :r_e], np.array(e["dB"], float)), got["dB"]
+            np.testing.assert_allclose(got["dm"][:d_oe], e["dm"], rtol=1e-6)
+            assert not got["dx"][:, d_ie:].any() and not got["dB"][d_oe:].any()
+
+
+
+# ---- small and ragged layers: full comparison ------------------------------------
+
+SMALL = [
+    ("tiny_f32", synth.CONFIGS["tiny_f32"], 0, {}),
+    ("tiny_f32_seed100", synth.CONFIGS["tiny_f32"], 100, {}),
+    ("tiny_f32_seed200", synth.CONFIGS["tiny_f32"], 200, {}),
+    ("tiny_as_bf16", synth.CONFIGS["tiny_f32"].replace(dtype="bf16"), 0, {}),
+    ("ragged_bf16", LayerShape(264, 520, 24, 37, 2.0, "bf16"), 1, {}),
+    ("ragged_f32", LayerShape(264, 520, 24, 37, 2.0, "f32"), 1, {}),
+    ("multitile_bf16", LayerShape(520, 1032, 136, 300, 2.0, "bf16"), 2, {}),
+    ("bigtile_ragged_bf16", LayerShape(776, 584, 72, 1031, 2.0, "bf16"), 3, {}),
+    ("minimal_bf16", LayerShape(8, 8, 8, 1, 2.0, "bf16"), 4, {}),
+    ("rank0_bf16", LayerShape(136, 200, 0, 19, 2.0, "bf16"), 5, {}),
+    ("rank0_f32", LayerShape(136, 200, 0, 19, 2.0, "f32"), 5, {}),
+    ("tokens0_bf16", LayerShape(136, 200, 16, 0, 2.0, "bf16"), 6, {}),
+    ("s0_bf16", LayerShape(136, 200, 16, 9, 0.0, "bf16"), 7, {}),
+    ("sneg_f32", LayerShape(136, 200, 16, 9, -0.75, "f32"), 8, {}),
+    ("largeB_bf16", LayerShape(264, 520, 24, 37, 2.0, "bf16"), 9, dict(b_std=0.1)),
+    ("zeroB_bf16", LayerShape(264, 520, 24, 37, 2.0, "bf16"), 10, dict(zero_b=True)),
+]
+
+
+@pytest.mark.parametrize("flags", [0, 2], ids=["fused", "separate"])
+@pytest.mark.parametrize("name,shape,seed,kw", SMALL, ids=[c[0] for c in SMALL])
+def test_small_parity(ops, name, shape, seed, kw, flags):
+    say(f"small parity {name} flags={flags} shape={shape}")
+    layer = synth.make_layer(shape, seed, grad=True, **kw)
+    got = run_layer(ops, shape, layer, flags=flags)
+    compare_full(shape, layer, got)
+    if kw.get("zero_b"):
+        assert not got["dA"].any(), "B = 0 gives dA = 0 exactly"
+
+
+def test_skip_outputs_and_recompute_xs(ops):
+    shape = LayerShape(264, 520, 24, 37, 2.0, "bf16")
+    layer = synth.make_layer(shape, 11, grad=True)
+    dev = layer_to_device(layer, "bf16")
+    y, norm, _ = ops.dora_forward(dev["x"], dev["W0"], dev["A"], dev["B"], dev["m"], shape.s,
+                                  keep_xs=False)
+    gx, gA, gB, gm = ops.dora_backward(dev["gy"], dev["x"], dev["W0"], dev["A"], dev["B"],
+                                       dev["m"], norm, None, y, shape.s, need=("B", "m"))
+    assert gx is None and gA is None
+    L = synth.layer_f64(layer, "bf16")
+    g = oracle.dora_backward(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
+    check_out(download(gB), g["dB"], "dB with xs recomputed")
+    check_out(download(gm), g["dm"], "dm")
+
+
+# ---- the crossover layer (2048 x 6144, r 64): full comparison ----------------------
+
+def test_crossover_parity(ops):
+    shape = synth.CONFIGS["crossover_bf16"]
+    for seed in (synth.CONFIG_SEED["crossover_bf16"], 100, 200):
+        say(f"crossover parity seed={seed}")
+        layer = synth.make_layer(shape, seed, grad=True)
+        for flags in (0, 2):
+            got = run_layer(ops, shape, layer, flags=flags, backward=(seed == 1))
+            compare_full(shape, layer, got, backward=(seed == 1))
+
+
+# ---- full-size layers: every norm, sampled outputs ----------------------------------
+
+def _sample(rng, n, k):
+    return rng.integers(0, n, size=k)
+
+
+@pytest.mark.parametrize("name", ["highrank_bf16", "widemlp_bf16"])
+def test_fullsize_forward_sampled(ops, name):
+    shape = synth.CONFIGS[name]
+    say(f"full-size forward {name}")
+    layer = synth.make_layer(shape, synth.CONFIG_SEED[name])
+    for flags in (0, 2):
+        got = run_layer(ops, shape, layer, flags=flags, backward=False)
+        L = layer
+        W0 = synth.to_f64(L["W0"], "bf16")
+        A = synth.to_f64(L["A"], "bf16")
+        B = synth.to_f64(L["B"], "bf16")
+        n_ref = oracle.dora_norm(W0, A, B, shape.s)
+        check_norm(got["norm"], n_ref, f"{name} norm (all rows)")
+        rng = np.random.Generator(np.random.PCG64(7))
+        tok = _sample(rng, shape.tokens, 4096)
+        rows = _sample(rng, shape.d_out, 4096)
+        tok[:8] = shape.tokens - 1
+        rows[:8] = np.arange(shape.d_out - 8, shape.d_out)
+        x = synth.to_f64(L["x"][np.unique(tok)], "bf16")
+        remap = {t: i for i, t in enumerate(np.unique(tok))}
+        m = synth.to_f64(L["m"], "bf16")
+        y_ref = oracle.dora_forward_entries(x, W0, A, B, m, shape.s,
+                                            np.array([remap[t] for t in tok]), rows)
+        check_out(got["y"][tok, rows], y_ref, f"{name} y (sampled)")
+        xs_ref = oracle.scaled_down_projection(x, A, shape.s)
+        check_out(got["xs"][np.unique(tok)], xs_ref, f"{name} xs (sampled tokens)")
+        del got
+
+
+def test_fullsize_backward_sampled(ops):
+    name = "highrank_bwd_bf16"
+    shape = synth.CONFIGS[name]
+    say(f"full-size backward {name}")
+    layer = synth.make_layer(shape, synth.CONFIG_SEED[name], grad=True)
+    got = run_layer(ops, shape, layer)
+    L = synth.layer_f64(layer, "bf16")
+    y_ref, n_ref = oracle.dora_forward(L["x"][:64], L["W0"], L["A"], L["B"], L["m"], shape.s)
+    check_norm(got["norm"], n_ref, "norm")
+    check_out(got["y"][:64], y_ref, "y (first 64 tokens)")
+    rng = np.random.Generator(np.random.PCG64(8))
+    tok = np.unique(_sample(rng, shape.tokens, 48))
+    rows = np.unique(_sample(rng, shape.d_out, 96))
+    cols = np.unique(_sample(rng, shape.d_in, 96))
+    tok[-1], rows[-1], cols[-1] = shape.tokens - 1, shape.d_out - 1, shape.d_in - 1
+    ref = oracle.dora_backward_sampled(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s,
+                                       tok, rows, cols)
+    check_out(got["dx"][tok], ref["dx"], "dx (sampled tokens)")
+    check_out(got["dB"][rows], ref["dB"], "dB (sampled rows)")
+    check_out(got["dA"][:, cols], ref["dA"], "dA (sampled columns)")
+    check_out(got["dm"][rows], ref["dm"], "dm (sampled rows)")
+
+
+# ---- the three norm terms, separated by flipping B ------------------------------------
+
+def test_norm_terms_separately(ops):
+    """n^2(B) - n^2(-B) = 2 cross and n^2(B) + n^2(-B) = 2 (base + Gram), with the
+    LoRA terms made comparable to the base term (B ~ N(0, 0.1^2))."""
+    shape = LayerShape(1024, 2048, 64, 1, 2.0, "bf16")
+    layer = synth.make_layer(shape, 12, b_std=0.1)
+    dev = layer_to_device(layer, "bf16")
+    n_p = download(ops.dora_norm(dev["W0"], dev["A"], dev["B"], shape.s))
+    n_m = download(ops.dora_norm(dev["W0"], dev["A"], (-dev["B"].float()).to(torch.bfloat16), shape.s))
+    L = synth.layer_f64(layer, "bf16")
+    base, cross, gram = oracle.norm_terms(L["W0"], L["A"], L["B"], shape.s)
+    say(f"cross/base ratio {np.abs(cross).mean() / base.mean():.3f}, gram/base {gram.mean() / base.mean():.3f}")
+    check_out((n_p ** 2 - n_m ** 2) / 2, cross, "cross term", atol_frac=1e-3, min_cos=0.99999)
+    check_out((n_p ** 2 + n_m ** 2) / 2, base + gram, "base + Gram", atol_frac=1e-4, min_cos=0.999999)
+    # B = 0 leaves the base term alone: n = ||W0_i||
+    n0 = download(ops.dora_norm(dev["W0"], dev["A"], torch.zeros_like(dev["B"]), shape.s))
+    check_norm(n0, np.sqrt(base), "B = 0 norm", rtol=1e-5)
+
+
+# ---- near-unity rescaling (float32 storage, so the output can show it) ---------------
+
+def test_near_unity_compose_f32(ops):
+    """m = n (1 + 1e-4): y - x W'^T must be far below the 1e-4 rescaling itself.
+
+    A compose that rounded g to a 16-bit float before subtracting 1 would be
+    off by ~2e-3 |y|; the near-unity form keeps the error at float32 level.
+    """
+    shape = LayerShape(512, 1024, 32, 64, 2.0, "f32")
+    layer = synth.make_layer(shape, 13)
+    L = synth.layer_f64(layer, "f32")
+    delta = 1e-4
+    n_ref = oracle.dora_norm(L["W0"], L["A"], L["B"], shape.s)
+    layer["m"] = (n_ref * (1 + delta)).astype(np.float32)
+    L["m"] = layer["m"].astype(np.float64)
+    y_ref, _ = oracle.dora_forward(L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
+    for flags in (0, 2):
+        got = run_layer(ops, shape, layer, flags=flags, backward=False)
+        err = np.max(np.abs(got["y"] - y_ref))
+        say(f"near-unity flags={flags}: max err {err:.3e} vs delta*max|y| {delta * np.max(np.abs(y_ref)):.3e}")
+        assert err <= 0.05 * delta * np.max(np.abs(y_ref))
+
+
+# ---- determinism, memory, timing hook, argument errors ---------------------------------
+
+def test_bitwise_deterministic(ops):
+    shape = LayerShape(1032, 2056, 72, 515, 2.0, "bf16")
+    layer = synth.make_layer(shape, 14, grad=True)
+    a = run_layer(ops, shape, layer)
+    b = run_layer(ops, shape, layer)
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k]), k
+
+
+def test_fused_and_separate_compose_agree(ops):
+    shape = LayerShape(1032, 2056, 72, 515, 2.0, "bf16")
+    layer = synth.make_layer(shape, 15)
+    f = run_layer(ops, shape, layer, flags=0, backward=False)
+    s = run_layer(ops, shape, layer, flags=2, backward=False)
+    assert np.array_equal(f["norm"], s["norm"])
+    err, scale, cos = out_stats(f["y"], s["y"])
+    assert err <= 2 ** -6 * scale and cos > 0.99999, (err, scale, cos)
+
+
+def test_no_dense_transient_memory(ops):
+    """Peak device memory of a headline-size forward + backward is inputs, outputs and
+    the declared workspace: no d_out x d_in buffer appears."""
+    shape = synth.CONFIGS["highrank_bf16"]
+    d_out, d_in, r, T = shape.d_out, shape.d_in, shape.r, shape.tokens
+    bf = torch.bfloat16
+    g = torch.Generator(device="cuda").manual_seed(0)
+    W0 = (torch.randn(d_out, d_in, device="cuda", generator=g) * 0.02).to(bf)
+    A = ((torch.rand(r, d_in, device="cuda", generator=g) * 2 - 1) / d_in ** 0.5).to(bf)
+    B = (torch.randn(d_out, r, device="cuda", generator=g) * 0.01).to(bf)
+    m = torch.linalg.vector_norm(W0.float(), dim=1).to(bf)
+    x = torch.randn(T, d_in, device="cuda", generator=g).to(bf)
+    gy = torch.randn(T, d_out, device="cuda", generator=g).to(bf)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    y, norm, xs = ops.dora_forward(x, W0, A, B, m, shape.s)
+    gx, gA, gB, gm = ops.dora_backward(gy, x, W0, A, B, m, norm, xs, y, shape.s)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    outputs = 2 * (T * d_out + T * r + T * d_in + r * d_in + d_out * r) + 8 * d_out
+    ws = sum(ops.workspace_bytes(d_out, d_in, r, T, bf, op) for op in (1, 2))
+    say(f"peak extra {peak / 1e6:.1f} MB; outputs {outputs / 1e6:.1f} MB; ws {ws / 1e6:.1f} MB; "
+        f"dense d_out x d_in bf16 would be {d_out * d_in * 2 / 1e6:.0f} MB")
+    assert peak <= outputs + ws + (32 << 20)
+    assert ws < d_out * d_in * 2 / 1.5
+
+
+def test_timing_hook(ops):
+    shape = LayerShape(264, 520, 24, 37, 2.0, "bf16")
+    layer = synth.make_layer(shape, 16, grad=True)
+    ops.timing_enable(True)
+    try:
+        run_layer(ops, shape, layer)
+        rec = ops.timing_collect()
+    finally:
+        ops.timing_enable(False)
+    for k in ("gram_AAt", "cross_gram_proj", "row_norm", "fused_fwd_gemm", "compose_bwd", "dx_gemm"):
+        assert k in rec and rec[k][0] >= 1 and rec[k][1] > 0, (k, rec)
+    assert ops.timing_collect() == {}
+
+
+def test_bad_arguments_raise_before_launch(ops):
+    from parameter_efficient_fine_dora_amd._lib import DoraError, ERR_CODE
+    W0 = torch.zeros(16, 17, dtype=torch.bfloat16, device="cuda")[:, 1:]
+    A = torch.zeros(8, 16, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(16, 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        ops.dora_norm(W0, A, B, 2.0)          # not contiguous (caught by the binding)
+    flat = torch.zeros(16 * 16 + 1, dtype=torch.bfloat16, device="cuda")
+    W0m = flat[1:].view(16, 16)               # contiguous but 2-byte misaligned
+    with pytest.raises(DoraError) as ei:
+        ops.dora_norm(W0m, A, B, 2.0)
+    assert ei.value.code == ERR_CODE["DORA_ERR_ALIGN"]
+    W0o = torch.zeros(16, 12, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(DoraError) as ei:
+        ops.dora_norm(W0o, torch.zeros(8, 12, dtype=torch.bfloat16, device="cuda"), B, 2.0)
+    assert ei.value.code == ERR_CODE["DORA_ERR_SHAPE"]
+
+
+def test_dora_linear_module(ops):
+    from parameter_efficient_fine_dora_amd.module import DoRALinear
+    shape = LayerShape(264, 520, 24, 37, 2.0, "bf16")
+    layer = synth.make_layer(shape, 17, grad=True)
+    dev = layer_to_device(layer, "bf16")
+    mod = DoRALinear(dev["W0"], shape.r, shape.s)
+    with torch.no_grad():
+        mod.A.copy_(dev["A"]); mod.B.copy_(dev["B"]); mod.m.copy_(dev["m"])
+    x = dev["x"].clone().requires_grad_(True)
+    y = mod(x.view(1, shape.tokens, shape.d_in)).view(shape.tokens, shape.d_out)
+    y.backward(dev["gy"])
+    L = synth.layer_f64(layer, "bf16")
+    y_ref, _ = oracle.dora_forward(L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
+    g = oracle.dora_backward(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
+    check_out(download(y), y_ref, "module y")
+    check_out(download(x.grad), g["dx"], "module dx")
+    check_out(download(mod.A.grad), g["dA"], "module dA")
+    check_out(download(mod.B.grad), g["dB"], "module dB")
+    check_out(download(mod.m.grad), g["dm"], "module dm")
+    # a fresh module starts at the pretrained point: B = 0, m = ||W0_i||, so y = x W0^T
+    fresh = DoRALinear(dev["W0"], shape.r, shape.s)
+    y0 = download(fresh(dev["x"]))
+    check_out(y0, L["x"] @ L["W0"].T, "fresh module y = x W0^T")
