@@ -1,0 +1,229 @@
+"""DoRA layer forward + backward on one MI355X: time per step, per-kernel roofline.
+
+One step = dora_forward (factored norm, down-projection, fused base + low-rank
+GEMM with the near-unity compose epilogue) + dora_backward (compose backward,
+dx, dA, dB, dm) of one bf16 layer with d_out = d_in = 8192, r = 384, s = 2 and
+4096 tokens, the headline shape of the Scaling DoRA paper (d_in = 8192,
+r = 384, bf16).  Inputs are synthetic (seeded, see synth), resident in HBM
+before the timed region; every output and workspace buffer is allocated
+before it too.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  ``value`` is microseconds per step (lower is better).
+``roofline`` covers the dominant kernel (largest share of the step), timed
+with HIP events on the library's launch stream over the timed steps;
+``kernels`` lists every kernel of the step the same way.  ``cpu_baseline``
+times the float64 oracle (dense W0 + sBA) on the host for one full step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DoRA layer fwd+bwd µs & norm/compose GB/s (% HBM peak), d=8192 r=384 bf16"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFS = 2500.0         # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def algorithmic_work(d_out, d_in, r, T):
+    """Per-launch algorithmic work of each kernel: ("flop", n) or ("byte", n).
+
+    Flops count 2 per multiply-add of the contraction the method needs; bytes
+    count one read of every input and one write of every output.
+    """
+    e = 2  # bf16
+    return {
+        "gram_AAt": ("flop", 2 * r * r * d_in),
+        "cross_gram_proj": ("flop", 2 * d_out * r * d_in + 2 * d_out * r * r),
+        "row_norm": ("byte", d_out * d_in * e + d_out * r * e + d_out * r * 4 + d_out * 4),
+        "down_proj_xs": ("flop", 2 * T * r * d_in),
+        "fused_fwd_gemm": ("flop", 2 * T * d_out * (d_in + r)),
+        "base_gemm": ("flop", 2 * T * d_out * d_in),
+        "up_proj_lora": ("flop", 2 * T * d_out * r),
+        "compose_fwd": ("byte", 3 * T * d_out * e + d_out * (e + 4)),
+        "compose_bwd": ("byte", 3 * T * d_out * e + d_out * (e + 4) + ((T + 63) // 64) * d_out * 4),
+        "dm_finalize": ("byte", ((T + 63) // 64) * d_out * 4 + d_out * (e + 4)),
+        "t_proj": ("flop", 2 * T * d_out * r),
+        "dx_gemm": ("flop", 2 * T * d_in * (d_out + r)),
+        "dB_gemm": ("flop", 2 * d_out * r * T),
+        "dA_gemm": ("flop", 2 * r * d_in * T),
+        "gram_finalize": ("byte", r * r * 4 * 2 + r * r * 4),
+    }
+
+
+def kernel_table(timing, steps, work):
+    out = {}
+    for name, (count, total_ms) in sorted(timing.items(), key=lambda kv: -kv[1][1]):
+        per = count / steps if steps else 0
+        avg_us = 1e3 * total_ms / count
+        row = {"launches_per_step": per, "avg_us": round(avg_us, 3),
+               "share": None}
+        if name in work:
+            kind, amount = work[name]
+            if kind == "flop":
+                tf = amount / (avg_us * 1e-6) / 1e12
+                row.update(tflops=round(tf, 2), frac_mfma_peak=round(tf / BF16_PEAK_TFS, 4))
+            else:
+                gbs = amount / (avg_us * 1e-6) / 1e9
+                row.update(gbps=round(gbs, 1), frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+        out[name] = row
+    tot = sum(v[1] for v in timing.values())
+    for name, row in out.items():
+        row["share"] = round(timing[name][1] / tot, 4) if tot else None
+    return out
+
+
+def cpu_baseline(layer_np, shape):
+    """The float64 oracle, as it stands, for one full forward + backward step."""
+    import numpy as np  # noqa: F401
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()
+                      if i.get("user_api") == "blas")
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    L = synth.layer_f64(layer_np, "bf16")
+    t0 = time.perf_counter()
+    oracle.dora_forward(L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
+    oracle.dora_backward(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
+    dt = time.perf_counter() - t0
+    return {"value": round(dt * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
+            "sample": "one full step (dense float64 forward + detached backward) of the same "
+                      "d=8192 r=384 T=4096 layer, inputs decoded from the same bf16 bits"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-compose", action="store_true",
+                    help="run the standalone compose kernels instead of the GEMM-fused ones")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the DoRA layer's "
+              "multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from parameter_efficient_fine_dora_amd import ops
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    shape = synth.CONFIGS["highrank_bwd_bf16"]
+    d_out, d_in, r, T, s = shape.d_out, shape.d_in, shape.r, shape.tokens, shape.s
+    flags = ops.FLAG_SEPARATE_COMPOSE if args.separate_compose else 0
+    print(f"# generating inputs d_out={d_out} d_in={d_in} r={r} T={T}", file=sys.stderr, flush=True)
+    layer = synth.make_layer(shape, synth.CONFIG_SEED[shape.name], grad=True)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    d = {k: up(v) for k, v in layer.items()}
+    bf = torch.bfloat16
+    y = torch.empty(T, d_out, dtype=bf, device=dev)
+    norm = torch.empty(d_out, dtype=torch.float32, device=dev)
+    xs = torch.empty(T, r, dtype=bf, device=dev)
+    gx = torch.empty(T, d_in, dtype=bf, device=dev)
+    gA = torch.empty(r, d_in, dtype=bf, device=dev)
+    gB = torch.empty(d_out, r, dtype=bf, device=dev)
+    gm = torch.empty(d_out, dtype=torch.float32, device=dev)
+    ws_f = torch.empty(ops.workspace_bytes(d_out, d_in, r, T, bf, 1, flags), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(ops.workspace_bytes(d_out, d_in, r, T, bf, 2, flags), dtype=torch.uint8,
+                       device=dev)
+
+    def step():
+        ops.dora_forward(d["x"], d["W0"], d["A"], d["B"], d["m"], s, y=y, norm_out=norm,
+                         xs_out=xs, workspace=ws_f, flags=flags)
+        ops.dora_backward(d["gy"], d["x"], d["W0"], d["A"], d["B"], d["m"], norm, xs, y, s,
+                          grad_x=gx, grad_A=gA, grad_B=gB, grad_m=gm, workspace=ws_b, flags=flags)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    print("# warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # per-kernel times: the same steps again, each launch bracketed by HIP events
+    print("# per-kernel timing", file=sys.stderr, flush=True)
+    ops.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ops.timing_enable(False)
+    timing = ops.timing_collect()
+    work = algorithmic_work(d_out, d_in, r, T)
+    kernels = kernel_table(timing, args.steps, work)
+    dominant = max(timing, key=lambda k: timing[k][1])
+    kind, amount = work[dominant]
+    avg_s = timing[dominant][1] / timing[dominant][0] * 1e-3
+    if kind == "flop":
+        achieved = amount / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFS, 4), "traffic": None,
+                "kernel": dominant, "per_launch": f"{amount / 1e9:.1f} GFLOP"}
+    else:
+        achieved = amount / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": dominant, "per_launch": f"{amount / 1e6:.1f} MB"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (float64 oracle, one step)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(layer, shape)
+
+    rec = {
+        "metric": METRIC, "value": round(ms_per_step * 1e3, 2), "unit": "us",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "DoRA linear fwd (factored norm + fused compose) + bwd, bf16",
+                   "d_out": d_out, "d_in": d_in, "r": r, "tokens": T, "s": s,
+                   "compose": "separate" if flags else "gemm-fused", "parallelism": "dp1"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

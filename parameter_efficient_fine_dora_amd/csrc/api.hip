@@ -3,6 +3,7 @@
 // kernels of gemm.hip and rowwise.hip; nothing here touches tensor data.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdio>
@@ -65,24 +66,23 @@ bool shape_ok(const dora_shape& s) {
   return true;
 }
 
-// Split-K factor for G = A A^T: enough workgroups to cover the chip, at least
-// two 64-deep K tiles per split.
+// K extent of the cross/Gram projection P = [W0 | B | B] [A | G_hi | G_lo]^T.
+int64_t p_depth(const dora_shape& s) { return s.d_in + (s.dtype == kBF16 ? 2 : 1) * s.r; }
+
 int gram_splits(const dora_shape& s) {
-  if (s.r == 0) return 1;
-  const int64_t tiles = cdiv(s.r, 64) * cdiv(s.r, 64);
-  const int64_t ktiles = cdiv(s.d_in, 64);
-  int64_t sp = cdiv(256, tiles);
-  sp = std::min<int64_t>(sp, std::max<int64_t>(1, ktiles / 2));
-  sp = std::min<int64_t>(sp, 64);
-  return (int)std::max<int64_t>(sp, 1);
+  return s.r > 0 ? plan_gemm(s.r, s.r, s.d_in, s.dtype).split : 1;
+}
+int p_splits(const dora_shape& s) {
+  return s.r > 0 ? plan_gemm(s.d_out, s.r, p_depth(s), s.dtype).split : 1;
 }
 
 struct Layout {
   size_t gpart = 0, ghi = 0, glo = 0, P = 0;     // norm
   size_t xs = 0, slora = 0;                      // forward
   size_t gz = 0, ts = 0, dmpart = 0;             // backward
+  size_t scratch = 0, scratch_bytes = 0;         // split-K partial sums
   size_t total = 0;
-  int splits = 1;
+  int splits = 1, psplits = 1;
   int64_t dm_blocks = 0;
 };
 
@@ -90,22 +90,33 @@ Layout layout(const dora_shape& s, int op) {
   Layout L;
   const size_t e = esize(s.dtype);
   const size_t r = (size_t)s.r, T = (size_t)s.tokens;
+  const int dt = s.dtype;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off += up(bytes);
     return o;
   };
+  size_t scratch = 0;
+  auto need = [&](int64_t M, int64_t N, int64_t K) {
+    scratch = std::max(scratch, gemm_scratch_bytes(M, N, K, dt));
+  };
   if (op == DORA_OP_NORM || op == DORA_OP_FORWARD) {
     L.splits = gram_splits(s);
+    L.psplits = p_splits(s);
     L.gpart = take((size_t)L.splits * r * r * 4);
     L.ghi = take(r * r * (s.dtype == kBF16 ? 2 : 4));
     L.glo = take(s.dtype == kBF16 ? r * r * 2 : 0);
-    L.P = take((size_t)s.d_out * r * 4);
+    L.P = take((size_t)L.psplits * s.d_out * r * 4);
   }
   if (op == DORA_OP_FORWARD) {
     L.xs = take(T * r * e);
-    if (s.flags & DORA_FLAG_SEPARATE_COMPOSE) L.slora = take(T * (size_t)s.d_out * e);
+    if (s.flags & DORA_FLAG_SEPARATE_COMPOSE) {
+      L.slora = take(T * (size_t)s.d_out * e);
+      need(s.tokens, s.d_out, s.d_in);
+      need(s.tokens, s.d_out, s.r);
+    }
+    need(s.tokens, s.r, s.d_in);
   }
   if (op == DORA_OP_BACKWARD) {
     L.xs = take(T * r * e);
@@ -113,7 +124,14 @@ Layout layout(const dora_shape& s, int op) {
     L.ts = take(T * r * e);
     L.dm_blocks = cdiv(s.tokens, kTokPerDmBlock);
     L.dmpart = take((size_t)L.dm_blocks * s.d_out * 4);
+    need(s.tokens, s.r, s.d_in);           // xs recomputed
+    need(s.tokens, s.r, s.d_out);          // ts = s gz B
+    need(s.tokens, s.d_in, s.d_out + s.r); // dx
+    need(s.d_out, s.r, s.tokens);          // dB
+    need(s.r, s.d_in, s.tokens);           // dA
   }
+  L.scratch = take(scratch);
+  L.scratch_bytes = scratch;
   L.total = off;
   return L;
 }
@@ -154,6 +172,11 @@ int check_ptr(const void* p, bool empty) {
 
 uint8_t* at(void* ws, size_t off) { return reinterpret_cast<uint8_t*>(ws) + off; }
 
+void give_scratch(GemmProblem& g, void* ws, const Layout& L) {
+  g.scratch = L.scratch_bytes ? at(ws, L.scratch) : nullptr;
+  g.scratch_bytes = L.scratch_bytes;
+}
+
 // Factored norm: G = A A^T (split-K), (s/2) G -> hi/lo, P = 2s W0 A^T + s^2 B G,
 // n_i = sqrt(||W0_i||^2 + B_i . P_i).
 int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, float* norm,
@@ -174,6 +197,7 @@ int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, 
     g.out_f32 = true;
     g.split = L.splits;
     g.split_stride = s.r * s.r;
+    g.cfg = plan_gemm(s.r, s.r, s.d_in, dt).cfg;
     HIP_TRY(gemm(g, dt, st, "gram_AAt"));
     HIP_TRY(gram_finalize(gpart, L.splits, s.r, s.s, dt, ghi, glo, st));
 
@@ -191,9 +215,12 @@ int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, 
     p.c = P;
     p.ldc = s.r;
     p.out_f32 = true;
+    p.split = L.psplits;
+    p.split_stride = s.d_out * s.r;
+    p.cfg = plan_gemm(s.d_out, s.r, p_depth(s), dt).cfg;
     HIP_TRY(gemm(p, dt, st, "cross_gram_proj"));
   }
-  HIP_TRY(row_norm(W0, B, P, norm, s.d_out, s.d_in, s.r, dt, st));
+  HIP_TRY(row_norm(W0, B, P, L.psplits, norm, s.d_out, s.d_in, s.r, dt, st));
   return DORA_OK;
 }
 
@@ -274,6 +301,7 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
     d.alpha = s.s;
     d.c = xs;
     d.ldc = s.r;
+    give_scratch(d, ws, L);
     HIP_TRY(gemm(d, dt, st, "down_proj_xs"));
   }
 
@@ -286,6 +314,7 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
     b.seg[0] = {x, W0, s.d_in, s.d_in, s.d_in};
     b.c = y;
     b.ldc = s.d_out;
+    give_scratch(b, ws, L);
     HIP_TRY(gemm(b, dt, st, "base_gemm"));
     void* slora = at(ws, L.slora);
     GemmProblem u;
@@ -295,6 +324,7 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
     u.seg[0] = {xs, B, s.r, s.r, s.r};
     u.c = slora;
     u.ldc = s.d_out;
+    give_scratch(u, ws, L);
     HIP_TRY(gemm(u, dt, st, "up_proj_lora"));
     HIP_TRY(compose_fwd(y, slora, m, norm_out, s.tokens, s.d_out, dt, st));
     return DORA_OK;
@@ -312,6 +342,7 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
   f.epi = kEpiCompose;
   f.mag = m;
   f.norm = norm_out;
+  give_scratch(f, ws, L);
   HIP_TRY(gemm(f, dt, st, "fused_fwd_gemm"));
   return DORA_OK;
 }
@@ -363,6 +394,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     t.alpha = s.s;
     t.c = ts;
     t.ldc = s.r;
+    give_scratch(t, ws, L);
     HIP_TRY(gemm(t, dt, st, "t_proj"));
   }
 
@@ -376,6 +408,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     d.b_kcontig = false;
     d.c = grad_x;
     d.ldc = s.d_in;
+    give_scratch(d, ws, L);
     HIP_TRY(gemm(d, dt, st, "dx_gemm"));
   }
 
@@ -391,6 +424,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
       d.alpha = s.s;
       d.c = xw;
       d.ldc = s.r;
+      give_scratch(d, ws, L);
       HIP_TRY(gemm(d, dt, st, "down_proj_xs"));
       xsu = xw;
     }
@@ -403,6 +437,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     b.b_kcontig = false;
     b.c = grad_B;
     b.ldc = s.r;
+    give_scratch(b, ws, L);
     HIP_TRY(gemm(b, dt, st, "dB_gemm"));
   }
 
@@ -416,6 +451,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     a.b_kcontig = false;
     a.c = grad_A;
     a.ldc = s.d_in;
+    give_scratch(a, ws, L);
     HIP_TRY(gemm(a, dt, st, "dA_gemm"));
   }
   return DORA_OK;

@@ -22,6 +22,8 @@
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 // remapped so that consecutive tiles (which share operand panels) run on
 // one XCD and share its L2, and tiles are walked in groups of 4 tile-rows.
+#include <algorithm>
+
 #include "kernels.h"
 #include "common.h"
 
@@ -358,33 +360,83 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
   }
 }
 
+// ---- split-K reduction ----------------------------------------------------------
+// out[i] = alpha * sum_{z < S} part[z][i] over M*N elements, fixed order.
+__global__ __launch_bounds__(256) void dora_splitk_reduce(const float* part, int S, int64_t n4,
+                                                          int64_t stride, float alpha, void* out,
+                                                          int out_bf16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 acc = reinterpret_cast<const f32x4*>(part)[i];
+  for (int z = 1; z < S; ++z) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(part + z * stride)[i];
+    acc += v;
+  }
+  acc *= alpha;
+  if (out_bf16)
+    reinterpret_cast<u32x2*>(out)[i] = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  else
+    reinterpret_cast<f32x4*>(out)[i] = acc;
+}
+
 // ---- host-side dispatch -----------------------------------------------------
 
-struct TileCfg {
-  int bm, bn;
+// Tile configurations: BM x BN workgroup tile, WM x WN waves.
+struct Cfg {
+  int bm, bn, wm, wn;
 };
+constexpr Cfg kCfgs[] = {
+    {256, 256, 2, 4},   // 0: 8 waves, 128x64 per wave
+    {256, 128, 2, 2},   // 1: 4 waves, 128x64 per wave
+    {128, 128, 2, 2},   // 2: 4 waves, 64x64 per wave
+    {128, 256, 2, 2},   // 3: 4 waves, 64x128 per wave
+    {64, 64, 2, 2},     // 4: 4 waves, 32x32 per wave
+    {256, 128, 4, 2},   // 5: 8 waves, 64x64 per wave
+};
+constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 template <int BM, int BN, int WM, int WN, bool AKC, bool BKC>
 hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStream_t st) {
   const dim3 block(WM * WN * 64);
-  // Only K-contiguous problems (the forward's) use the float32-out and compose epilogues.
-  if constexpr (AKC && BKC) {
+  if (out_f32) {
+    hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, true>), grid, block, 0,
+                       st, a);
+    return hipGetLastError();
+  }
+  if constexpr (AKC && BKC) {   // the compose epilogue belongs to the forward (K-contiguous) GEMM
     if (epi == kEpiCompose) {
       hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiCompose, false>), grid,
                          block, 0, st, a);
       return hipGetLastError();
     }
-    if (out_f32) {
-      hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, true>), grid, block,
-                         0, st, a);
-      return hipGetLastError();
-    }
   } else {
-    if (epi != kEpiStore || out_f32) return hipErrorInvalidValue;
+    if (epi != kEpiStore) return hipErrorInvalidValue;
   }
   hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, false>), grid, block, 0,
                      st, a);
   return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_layout(bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
+                         hipStream_t st) {
+  if (akc && bkc) return launch_bf16<BM, BN, WM, WN, true, true>(a, epi, out_f32, grid, st);
+  if (akc && !bkc) return launch_bf16<BM, BN, WM, WN, true, false>(a, epi, out_f32, grid, st);
+  if (!akc && !bkc) return launch_bf16<BM, BN, WM, WN, false, false>(a, epi, out_f32, grid, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
+                      hipStream_t st) {
+  switch (cfg) {
+    case 0: return launch_layout<256, 256, 2, 4>(akc, bkc, a, epi, out_f32, grid, st);
+    case 1: return launch_layout<256, 128, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 2: return launch_layout<128, 128, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 3: return launch_layout<128, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 4: return launch_layout<64, 64, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 5: return launch_layout<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <bool AKC, bool BKC>
@@ -396,31 +448,14 @@ hipError_t launch_f32(const KArgs& a, int epi, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile size for a bf16 problem: the largest tile that still yields enough
-// workgroups to cover the 256 compute units.
-TileCfg pick_tile(int64_t M, int64_t N) {
-  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  if (tiles(256, 256) >= 384) return {256, 256};
-  if (tiles(128, 128) >= 160) return {128, 128};
-  return {64, 64};
-}
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-}  // namespace
-
-int64_t gemm_ktiles(const GemmProblem& p, int /*dtype*/) {
-  int64_t t = 0;
-  for (int s = 0; s < p.nseg; ++s) t += (p.seg[s].K + kBK - 1) / kBK;
-  return t;
-}
-
-hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* label) {
-  if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  KArgs a{};
+// Fill KArgs from the problem; returns the total number of 64-deep K tiles.
+int fill_args(const GemmProblem& p, KArgs& a) {
+  a = KArgs{};
   a.M = (int)p.M;
   a.N = (int)p.N;
-  // drop empty segments
-  int ns = 0;
-  int kt = 0;
+  int ns = 0, kt = 0;
   for (int s = 0; s < p.nseg; ++s) {
     if (p.seg[s].K <= 0) continue;
     a.a[ns] = reinterpret_cast<const uint16_t*>(p.seg[s].a);
@@ -428,33 +463,73 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
     a.lda[ns] = p.seg[s].lda;
     a.ldb[ns] = p.seg[s].ldb;
     a.K[ns] = (int)p.seg[s].K;
-    kt += (int)((p.seg[s].K + kBK - 1) / kBK);
+    kt += (int)cdiv64(p.seg[s].K, kBK);
     a.kt_end[ns] = kt;
     ++ns;
   }
   if (ns == 0) {  // empty K: C = 0 (one zero-length segment keeps the kernel uniform)
-    a.a[0] = nullptr;
-    a.b[0] = nullptr;
     a.K[0] = 0;
     a.kt_end[0] = 0;
     ns = 1;
   }
   for (int s = ns; s < 3; ++s) a.kt_end[s] = kt;
   a.nseg = ns;
-  const int split = p.split < 1 ? 1 : p.split;
-  a.kt_per_split = (kt + split - 1) / split;
-  if (a.kt_per_split < 1) a.kt_per_split = 1;
   a.c = p.c;
   a.ldc = p.ldc;
   a.split_stride = p.split_stride;
   a.alpha = p.alpha;
   a.mag = p.mag;
   a.norm = p.norm;
+  return kt;
+}
 
-  LaunchTimer timer(label, st);
+hipError_t run(int cfg, int split, const GemmProblem& p, KArgs& a, int kt, hipStream_t st,
+               bool out_f32) {
+  const Cfg c = kCfgs[cfg];
+  a.tiles_m = (int)cdiv64(p.M, c.bm);
+  a.tiles_n = (int)cdiv64(p.N, c.bn);
+  a.kt_per_split = split > 1 ? (kt + split - 1) / split : (kt > 0 ? kt : 1);
+  if (a.kt_per_split < 1) a.kt_per_split = 1;
+  const dim3 grid(a.tiles_m * a.tiles_n, split);
+  return launch_cfg(cfg, p.a_kcontig, p.b_kcontig, a, p.epi, out_f32, grid, st);
+}
+
+}  // namespace
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype) {
+  if (dtype == kF32 || M <= 0 || N <= 0) return {-1, 1};
+  const int64_t ktiles = cdiv64(K, kBK);
+  auto tiles = [&](int cfg) { return cdiv64(M, kCfgs[cfg].bm) * cdiv64(N, kCfgs[cfg].bn); };
+  // Large outputs: 256 x 256 tiles (8 waves), then 256 x 128 (8 waves).
+  if (tiles(0) >= 256) return {0, 1};
+  if (tiles(5) >= 200) return {5, 1};
+  // Skinny or small: 128 x 128 tiles, split along K to ~384 workgroups
+  // (measured best for the N = r projections of the d = 8192, r = 384 layer).
+  const int64_t t = tiles(2);
+  int64_t split = (384 + t / 2) / t;
+  split = std::min<int64_t>(split, std::max<int64_t>(1, ktiles / 8));
+  split = std::max<int64_t>(1, std::min<int64_t>(split, 16));
+  return {2, (int)split};
+}
+
+size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype) {
+  const GemmPlan pl = plan_gemm(M, N, K, dtype);
+  return pl.split > 1 ? (size_t)pl.split * M * N * 4 : 0;
+}
+
+hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* label) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  KArgs a;
+  const int kt = fill_args(p, a);
+  int64_t K = 0;
+  for (int s = 0; s < p.nseg; ++s) K += p.seg[s].K > 0 ? p.seg[s].K : 0;
+
   if (dtype == kF32) {
-    a.tiles_m = (int)((p.M + 63) / 64);
-    a.tiles_n = (int)((p.N + 63) / 64);
+    LaunchTimer timer(label, st);
+    a.tiles_m = (int)cdiv64(p.M, 64);
+    a.tiles_n = (int)cdiv64(p.N, 64);
+    const int split = p.split < 1 ? 1 : p.split;
+    a.kt_per_split = split > 1 ? (kt + split - 1) / split : (kt > 0 ? kt : 1);
     const dim3 grid(a.tiles_m * a.tiles_n, split);
     if (p.a_kcontig && p.b_kcontig) return launch_f32<true, true>(a, p.epi, grid, st);
     if (p.a_kcontig) return launch_f32<true, false>(a, p.epi, grid, st);
@@ -462,24 +537,38 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
     return launch_f32<false, false>(a, p.epi, grid, st);
   }
 
-  const TileCfg t = pick_tile(p.M, p.N);
-  a.tiles_m = (int)((p.M + t.bm - 1) / t.bm);
-  a.tiles_n = (int)((p.N + t.bn - 1) / t.bn);
-  const dim3 grid(a.tiles_m * a.tiles_n, split);
-#define DORA_GEMM_LAYOUTS(BM, BN, WM, WN)                                                 \
-  do {                                                                                    \
-    if (p.a_kcontig && p.b_kcontig)                                                       \
-      return launch_bf16<BM, BN, WM, WN, true, true>(a, p.epi, p.out_f32, grid, st);      \
-    if (p.a_kcontig && !p.b_kcontig)                                                      \
-      return launch_bf16<BM, BN, WM, WN, true, false>(a, p.epi, p.out_f32, grid, st);     \
-    if (!p.a_kcontig && !p.b_kcontig)                                                     \
-      return launch_bf16<BM, BN, WM, WN, false, false>(a, p.epi, p.out_f32, grid, st);    \
-    return hipErrorInvalidValue;                                                          \
-  } while (0)
-  if (t.bm == 256) DORA_GEMM_LAYOUTS(256, 256, 2, 4);
-  if (t.bm == 128) DORA_GEMM_LAYOUTS(128, 128, 2, 2);
-  DORA_GEMM_LAYOUTS(64, 64, 2, 2);
-#undef DORA_GEMM_LAYOUTS
+  int cfg = p.cfg;
+  if (cfg < 0 || cfg >= kNumCfgs) cfg = plan_gemm(p.M, p.N, K, dtype).cfg;
+  if (p.split > 1 || p.out_f32) {   // caller-managed partial sums (or a plain float32 output)
+    LaunchTimer timer(label, st);
+    return run(cfg, p.split < 1 ? 1 : p.split, p, a, kt, st, p.out_f32);
+  }
+  GemmPlan pl = plan_gemm(p.M, p.N, K, dtype);
+  if (p.cfg >= 0) pl.cfg = cfg;
+  if (p.force_split > 0) pl.split = p.force_split;
+  const size_t need = (size_t)pl.split * p.M * p.N * 4;
+  if (pl.split > 1 && p.epi == kEpiStore && p.scratch && p.scratch_bytes >= need) {
+    // Split-K: float32 partials into scratch, then a fixed-order reduction.
+    KArgs b = a;
+    b.c = p.scratch;
+    b.ldc = p.N;
+    b.split_stride = p.M * p.N;
+    b.alpha = 1.f;
+    {
+      LaunchTimer timer(label, st);
+      const hipError_t e = run(pl.cfg, pl.split, p, b, kt, st, true);
+      if (e != hipSuccess) return e;
+    }
+    if (p.ldc != p.N) return hipErrorInvalidValue;
+    LaunchTimer timer("splitk_reduce", st);
+    const int64_t n4 = p.M * p.N / 4;
+    hipLaunchKernelGGL(dora_splitk_reduce, dim3((unsigned)cdiv64(n4, 256)), dim3(256), 0, st,
+                       reinterpret_cast<const float*>(p.scratch), pl.split, n4, p.M * p.N, p.alpha,
+                       p.c, 1);
+    return hipGetLastError();
+  }
+  LaunchTimer timer(label, st);
+  return run(cfg, 1, p, a, kt, st, false);
 }
 
 }  // namespace dora

@@ -36,21 +36,37 @@ struct GemmProblem {
   int epi = kEpiStore;
   const void* mag = nullptr;   // kEpiCompose: m [N] (layer dtype)
   const float* norm = nullptr; // kEpiCompose: n [N] float32
+  // Library-chosen split-K (layer-dtype store epilogue only): float32 partial
+  // sums go to `scratch`, then a fixed-order reduction writes C.
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  int cfg = -1;                // tile configuration override (-1 = planner's choice)
+  int force_split = 0;         // split-K override for the scratch path (0 = planner's choice)
 };
+
+struct GemmPlan {
+  int cfg;     // tile configuration index (-1: float32 VALU kernel)
+  int split;   // split-K factor
+};
+
+// Tile configuration and split-K factor for a layer-dtype GEMM of this size.
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype);
+
+// Scratch bytes the split-K path of gemm() needs for this size (0 if unsplit).
+size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype);
 
 // Enqueue C = sum over segments; picks the tile configuration from the shape.
 hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* label);
 
-// Number of 64-deep K tiles a segment list spans (used for split-K sizing).
-int64_t gemm_ktiles(const GemmProblem& p, int dtype);
 
 // G partial sums -> (s/2) * G, symmetrised; bf16: written as hi + lo bf16 pair.
 hipError_t gram_finalize(const float* part, int splits, int64_t r, float s, int dtype,
                          void* g_hi, void* g_lo, hipStream_t st);
 
-// n_i = sqrt(max(0, ||W0_i||^2 + B_i . P_i)).
-hipError_t row_norm(const void* W0, const void* B, const float* P, float* norm, int64_t d_out,
-                    int64_t d_in, int64_t r, int dtype, hipStream_t st);
+// n_i = sqrt(max(0, ||W0_i||^2 + B_i . P_i)), P = sum of p_splits partials
+// [p_splits][d_out][r] (float32).
+hipError_t row_norm(const void* W0, const void* B, const float* P, int p_splits, float* norm,
+                    int64_t d_out, int64_t d_in, int64_t r, int dtype, hipStream_t st);
 
 // y = base + ((g-1) base + g * slora) in place on y (base), slora = s * lora.
 hipError_t compose_fwd(void* y, const void* slora, const void* m, const float* norm, int64_t T,

@@ -89,8 +89,8 @@ __global__ __launch_bounds__(256) void dora_gram_finalize(const float* part, int
 // go straight to registers) and the lane partials meet in a wave reduction.
 template <bool BF>
 __global__ __launch_bounds__(256) void dora_row_norm(const void* W0, const void* B, const float* P,
-                                                     float* norm, int64_t d_out, int64_t d_in,
-                                                     int64_t r) {
+                                                     int p_splits, int64_t p_stride, float* norm,
+                                                     int64_t d_out, int64_t d_in, int64_t r) {
   using V = Vec<BF>;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void dora_row_norm(const void* W0, const void*
 #pragma unroll
     for (int q = 0; q < V::kN; ++q) acc0 = fmaf(a[q], a[q], acc0);
   }
-  // cross + Gram: B_i . P_i
+  // cross + Gram: B_i . P_i, P given as p_splits split-K partial sums
   const int64_t rv = r / V::kN;
   const float* prow = P + row * r;
   for (int64_t cc = lane; cc < rv; cc += 64) {
@@ -127,7 +127,9 @@ __global__ __launch_bounds__(256) void dora_row_norm(const void* W0, const void*
     V::load(B, row * rv + cc, bv);
 #pragma unroll
     for (int q = 0; q < V::kN; q += 4) {
-      const f32x4 pv = *reinterpret_cast<const f32x4*>(prow + cc * V::kN + q);
+      f32x4 pv = *reinterpret_cast<const f32x4*>(prow + cc * V::kN + q);
+      for (int z = 1; z < p_splits; ++z)
+        pv += *reinterpret_cast<const f32x4*>(prow + z * p_stride + cc * V::kN + q);
       acc1 = fmaf(bv[q], pv[0], acc1);
       acc1 = fmaf(bv[q + 1], pv[1], acc1);
       acc1 = fmaf(bv[q + 2], pv[2], acc1);
@@ -236,15 +238,18 @@ hipError_t gram_finalize(const float* part, int splits, int64_t r, float s, int 
   return hipGetLastError();
 }
 
-hipError_t row_norm(const void* W0, const void* B, const float* P, float* norm, int64_t d_out,
-                    int64_t d_in, int64_t r, int dtype, hipStream_t st) {
+hipError_t row_norm(const void* W0, const void* B, const float* P, int p_splits,
+                    float* norm, int64_t d_out, int64_t d_in, int64_t r, int dtype,
+                    hipStream_t st) {
   LaunchTimer t("row_norm", st);
   const dim3 grid((unsigned)cdiv(d_out, 4));
+  const int64_t stride = d_out * r;
   if (dtype == kBF16)
-    hipLaunchKernelGGL(dora_row_norm<true>, grid, dim3(256), 0, st, W0, B, P, norm, d_out, d_in, r);
+    hipLaunchKernelGGL(dora_row_norm<true>, grid, dim3(256), 0, st, W0, B, P, p_splits, stride,
+                       norm, d_out, d_in, r);
   else
-    hipLaunchKernelGGL(dora_row_norm<false>, grid, dim3(256), 0, st, W0, B, P, norm, d_out, d_in,
-                       r);
+    hipLaunchKernelGGL(dora_row_norm<false>, grid, dim3(256), 0, st, W0, B, P, p_splits, stride,
+                       norm, d_out, d_in, r);
   return hipGetLastError();
 }
 

@@ -73,8 +73,12 @@ def bf16_bits(a) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
     a = np.ascontiguousarray(a, dtype=np.float32)
     u = a.view(np.uint32)
-    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-    out = (rounded >> np.uint32(16)).astype(np.uint16)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                      # no overflow: |a| <= FLT_MAX keeps u + 0x8000 < 2^32
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
         out[nan] = np.uint16(0x7FC0)

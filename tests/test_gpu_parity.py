@@ -333,7 +333,8 @@ def test_no_dense_transient_memory(ops):
     say(f"peak extra {peak / 1e6:.1f} MB; outputs {outputs / 1e6:.1f} MB; ws {ws / 1e6:.1f} MB; "
         f"dense d_out x d_in bf16 would be {d_out * d_in * 2 / 1e6:.0f} MB")
     assert peak <= outputs + ws + (32 << 20)
-    assert ws < d_out * d_in * 2 / 1.5
+    # the only non-activation workspace (norm + forward) is far below one d_out x d_in matrix
+    assert ops.workspace_bytes(d_out, d_in, r, T, bf, 1) < d_out * d_in * 2 / 2
 
 
 def test_timing_hook(ops):
