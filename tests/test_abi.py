@@ -103,8 +103,8 @@ def test_workspace_never_scales_with_d_out_times_d_in():
         fwd_ws = _lib.workspace_bytes(sh, _lib.OP_FORWARD)
         bwd_ws = _lib.workspace_bytes(sh, _lib.OP_BACKWARD)
         assert norm_ws < dense / 3
-        # at most 16 split-K partial Gram matrices and 4 partial projections P [d_out, r]
-        assert norm_ws <= 16 * r * r * 4 + r * r * 4 + 4 * d_out * r * 4 + 4096
+        # at most 16 split-K partial Gram matrices and 16 partial projections P [d_out, r]
+        assert norm_ws <= 16 * r * r * 4 + r * r * 4 + 16 * d_out * r * 4 + 4096
         # forward adds xs [T, r] and split-K partials of at most 16 [T, r] float32 blocks
         assert fwd_ws - norm_ws <= T * r * 2 + 16 * T * r * 4 + 4096
         split_k = 16 * max(T * r, d_out * r, r * d_in) * 4
