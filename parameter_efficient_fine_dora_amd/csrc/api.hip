@@ -98,8 +98,8 @@ Layout layout(const dora_shape& s, int op) {
     return o;
   };
   size_t scratch = 0;
-  auto need = [&](int64_t M, int64_t N, int64_t K) {
-    scratch = std::max(scratch, gemm_scratch_bytes(M, N, K, dt));
+  auto need = [&](int64_t M, int64_t N, int64_t K, bool akc = true, bool bkc = true) {
+    scratch = std::max(scratch, gemm_scratch_bytes(M, N, K, dt, akc, bkc));
   };
   if (op == DORA_OP_NORM || op == DORA_OP_FORWARD) {
     L.splits = gram_splits(s);
@@ -124,11 +124,11 @@ Layout layout(const dora_shape& s, int op) {
     L.ts = take(T * r * e);
     L.dm_blocks = cdiv(s.tokens, kTokPerDmBlock);
     L.dmpart = take((size_t)L.dm_blocks * s.d_out * 4);
-    need(s.tokens, s.r, s.d_in);           // xs recomputed
-    need(s.tokens, s.r, s.d_out);          // ts = s gz B
-    need(s.tokens, s.d_in, s.d_out + s.r); // dx
-    need(s.d_out, s.r, s.tokens);          // dB
-    need(s.r, s.d_in, s.tokens);           // dA
+    need(s.tokens, s.r, s.d_in);                         // xs recomputed
+    need(s.tokens, s.r, s.d_out, true, false);           // ts = s gz B
+    need(s.tokens, s.d_in, s.d_out + s.r, true, false);  // dx
+    need(s.d_out, s.r, s.tokens, false, false);          // dB
+    need(s.r, s.d_in, s.tokens, false, false);           // dA
   }
   L.scratch = take(scratch);
   L.scratch_bytes = scratch;

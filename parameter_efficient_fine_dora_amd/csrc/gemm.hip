@@ -41,6 +41,7 @@ struct KArgs {
   int64_t lda[3], ldb[3];
   int K[3];
   int kt_end[3];         // cumulative number of K tiles after each segment
+  int kt_total;          // kt_end[nseg - 1], kept apart so no array is indexed at run time
   int kt_per_split;
   int tiles_m, tiles_n;
   void* c;
@@ -53,25 +54,75 @@ struct KArgs {
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
 
+// ---- buffer resources ---------------------------------------------------------
+// Operands are read through raw buffer resources rebased at the current tile,
+// so out-of-range rows (and K tails, sent to kOob) come back as zeros from the
+// hardware range check instead of through branches.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;   // offset beyond every record: the load returns 0
+constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) buffer, gfx9-family data format
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  const int64_t b = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)b, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Operand views of one K segment (wave-uniform).
+struct OpView {
+  const uint16_t* p;
+  int64_t ld;
+  int K;
+};
+
 // ---- global -> LDS copies ---------------------------------------------------
 
-// K-contiguous operand: R rows x 64 k, one 16-byte chunk (8 k) per copy.
+// K-contiguous operand, R rows x 64 k, copied straight into LDS with
+// buffer_load ... lds: one wave instruction fills 8 rows x 128 B, lane l
+// takes row l/8 and physical chunk l%8, i.e. logical chunk (l%8) ^ swz(row).
+template <int R, int NW>
+struct DmaKC {
+  static constexpr int kInstr = R / 8 / NW;   // per wave
+  static_assert(R % (8 * NW) == 0, "rows must split evenly over the waves");
+  __device__ __forceinline__ static void issue(uint8_t* lds_tile, const OpView& v, int row0,
+                                               int nrows, int k0, int wave, int lane) {
+    int64_t rows = nrows - row0;
+    if (rows > R) rows = R;
+    const Rsrc rs = make_rsrc(v.p + (int64_t)row0 * v.ld, rows * v.ld * 2);
+#pragma unroll
+    for (int i = 0; i < kInstr; ++i) {
+      const int rbase = (wave * kInstr + i) * 8;
+      const int row = rbase + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(row);
+      const int gk = k0 + kc * 8;
+      // 32-bit arithmetic: a tile spans < 2^31 bytes (the library limits every dimension)
+      const uint32_t off = gk < v.K ? (uint32_t)row * (uint32_t)(v.ld * 2) + (uint32_t)gk * 2u : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds_tile + rbase * kRowBytes), 16, (int)off,
+          0, 0, 0);
+    }
+  }
+};
+
+// K-contiguous operand through registers: one 16-byte chunk (8 k) per copy.
 template <int R, int NT>
-struct LoadKC {
+struct RegKC {
   static constexpr int kChunks = R * 8;
   static constexpr int kPer = (kChunks + NT - 1) / NT;
   u32x4 v[kPer];
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t ld, int row0, int nrows,
-                                       int k0, int K, int tid) {
+  __device__ __forceinline__ void load(const OpView& o, int row0, int nrows, int k0, int tid) {
+    int64_t rows = nrows - row0;
+    if (rows > R) rows = R;
+    const Rsrc rs = make_rsrc(o.p + (int64_t)row0 * o.ld, rows * o.ld * 2);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int c = tid + i * NT;
       const int row = c >> 3, kc = c & 7;
-      const int gr = row0 + row, gk = k0 + kc * 8;
-      if ((kChunks % NT == 0 || c < kChunks) && gr < nrows && gk < K)
-        v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)gr * ld + gk);
-      else
-        v[i] = u32x4{0u, 0u, 0u, 0u};
+      const int gk = k0 + kc * 8;
+      const bool ok = (kChunks % NT == 0 || c < kChunks) && gk < o.K;
+      v[i] = bload16(rs, ok ? (uint32_t)row * (uint32_t)(o.ld * 2) + (uint32_t)gk * 2u : kOob);
     }
   }
   __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
@@ -85,30 +136,41 @@ struct LoadKC {
   }
 };
 
-// M/N-contiguous operand: element (row, k) at base[k*ld + row].  Copied as
+// M/N-contiguous operand: element (row, k) at p[k*ld + row].  Copied as
 // blocks of 4 consecutive k x 8 consecutive rows (four 16-byte loads),
 // transposed in registers into eight 8-byte row pieces.
 template <int R, int NT>
-struct LoadMC {
+struct RegMC {
   static constexpr int kRowChunks = R / 8;
   static constexpr int kBlocks = kRowChunks * (kBK / 4);
   static constexpr int kPer = (kBlocks + NT - 1) / NT;
+  static_assert(kRowChunks % 8 == 0, "block order assumes a multiple of 64 rows");
   u32x4 v[kPer][4];
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t ld, int row0, int nrows,
-                                       int k0, int K, int tid) {
+  // Block b -> (k-quad kq, row-chunk rc): eight consecutive blocks take eight
+  // consecutive row chunks and the next eight the other half of the same
+  // 16-byte k chunk, so sixteen lanes' 8-byte LDS writes fill sixteen distinct
+  // bank slots, while each eight lanes still read 128 contiguous bytes.
+  __device__ __forceinline__ static void block_of(int b, int& kq, int& rc) {
+    const int lo = b & 7, kh = (b >> 3) & 1, rest = b >> 4;
+    constexpr int kHi = kRowChunks / 8;
+    rc = (rest % kHi) * 8 + lo;
+    kq = (rest / kHi) * 2 + kh;
+  }
+  __device__ __forceinline__ void load(const OpView& o, int row0, int nrows, int k0, int tid) {
+    int64_t krows = o.K - k0;
+    if (krows > kBK) krows = kBK;
+    // rebased at (k0, row0); rows k >= K fall past the end of the records
+    const Rsrc rs = make_rsrc(o.p + (int64_t)k0 * o.ld + row0, krows * o.ld * 2 - (int64_t)row0 * 2);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int b = tid + i * NT;
-      const int kq = b / kRowChunks, rc = b - kq * kRowChunks;
-      const int gr = row0 + rc * 8;
-      const bool ok = (kBlocks % NT == 0 || b < kBlocks) && gr < nrows;
+      int kq, rc;
+      block_of(b, kq, rc);
+      const bool ok = (kBlocks % NT == 0 || b < kBlocks) && row0 + rc * 8 < nrows;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int gk = k0 + kq * 4 + j;
-        if (ok && gk < K)
-          v[i][j] = *reinterpret_cast<const u32x4*>(base + (int64_t)gk * ld + gr);
-        else
-          v[i][j] = u32x4{0u, 0u, 0u, 0u};
+        const int kl = kq * 4 + j;
+        v[i][j] = bload16(rs, ok ? (uint32_t)kl * (uint32_t)(o.ld * 2) + (uint32_t)rc * 16u : kOob);
       }
     }
   }
@@ -117,7 +179,8 @@ struct LoadMC {
     for (int i = 0; i < kPer; ++i) {
       const int b = tid + i * NT;
       if (kBlocks % NT != 0 && b >= kBlocks) continue;
-      const int kq = b / kRowChunks, rc = b - kq * kRowChunks;
+      int kq, rc;
+      block_of(b, kq, rc);
       const int chunk = kq >> 1, half = kq & 1;
 #pragma unroll
       for (int mm = 0; mm < 8; ++mm) {
@@ -139,76 +202,108 @@ struct LoadMC {
   }
 };
 
+// Per-operand copy policy: K-contiguous operands go global -> LDS directly,
+// M/N-contiguous ones through registers (they are transposed on the way).
 template <int R, int NT, bool KC>
-struct Loader;
+struct Copier;
 template <int R, int NT>
-struct Loader<R, NT, true> : LoadKC<R, NT> {};
+struct Copier<R, NT, true> {
+  static constexpr bool kDirect = true;
+  __device__ __forceinline__ void issue(uint8_t* lds, const OpView& o, int row0, int nrows, int k0,
+                                        int tid, int wave, int lane) {
+    DmaKC<R, NT / 64>::issue(lds, o, row0, nrows, k0, wave, lane);
+  }
+  __device__ __forceinline__ void commit(uint8_t*, int) {}
+};
 template <int R, int NT>
-struct Loader<R, NT, false> : LoadMC<R, NT> {};
+struct Copier<R, NT, false> {
+  static constexpr bool kDirect = false;
+  RegMC<R, NT> r;
+  __device__ __forceinline__ void issue(uint8_t*, const OpView& o, int row0, int nrows, int k0,
+                                        int tid, int, int) {
+    r.load(o, row0, nrows, k0, tid);
+  }
+  __device__ __forceinline__ void commit(uint8_t* lds, int tid) { r.store(lds, tid); }
+};
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* lds, int row, int chunk) {
   return *reinterpret_cast<const bf16x8*>(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4));
 }
 
 // Tile index -> (tile_m, tile_n), XCD-grouped, 4 tile-rows per group.
-__device__ __forceinline__ void tile_coords(const KArgs& p, int& tm, int& tn) {
+// Returns tile_m in .x and tile_n in .y.
+__device__ __forceinline__ int2 tile_coords(int tiles_m, int tiles_n) {
   int L = blockIdx.x;
   const int nwg = gridDim.x;
   if ((nwg & 7) == 0) L = (L & 7) * (nwg >> 3) + (L >> 3);
   constexpr int kGroup = 4;
-  const int per_group = kGroup * p.tiles_n;
+  const int per_group = kGroup * tiles_n;
   const int g = L / per_group;
   const int first = g * kGroup;
-  const int gsz = min(p.tiles_m - first, kGroup);
+  const int gsz = min(tiles_m - first, kGroup);
   const int rem = L - g * per_group;
-  tm = first + rem % gsz;
-  tn = rem / gsz;
+  return make_int2(first + rem % gsz, rem / gsz);
 }
 
 template <bool OUT_F32>
-__device__ __forceinline__ void store4(const KArgs& p, void* cbase, int m, int n, float v0,
-                                       float v1, float v2, float v3) {
+__device__ __forceinline__ void store4(void* cbase, int64_t ldc, int m, int n, float v0, float v1,
+                                       float v2, float v3) {
   if (OUT_F32) {
-    float* c = reinterpret_cast<float*>(cbase) + (int64_t)m * p.ldc + n;
+    float* c = reinterpret_cast<float*>(cbase) + (int64_t)m * ldc + n;
     *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
   } else {
-    uint16_t* c = reinterpret_cast<uint16_t*>(cbase) + (int64_t)m * p.ldc + n;
+    uint16_t* c = reinterpret_cast<uint16_t*>(cbase) + (int64_t)m * ldc + n;
     *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
   }
 }
 
 // g - 1 for output columns n..n+3 (compose epilogue).
 template <bool BF>
-__device__ __forceinline__ f32x4 gm1_4(const KArgs& p, int n) {
+__device__ __forceinline__ f32x4 gm1_4(const void* mag, const float* norm, int n) {
   f32x4 r;
-  const float* nr = p.norm + n;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float mv = BF ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.mag)[n + e])
-                        : reinterpret_cast<const float*>(p.mag)[n + e];
-    const float nv = fmaxf(nr[e], kNormEps);
+    const float mv = BF ? bf16_to_f32(reinterpret_cast<const uint16_t*>(mag)[n + e])
+                        : reinterpret_cast<const float*>(mag)[n + e];
+    const float nv = fmaxf(norm[n + e], kNormEps);
     r[e] = (mv - nv) / nv;
   }
   return r;
 }
 
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32>
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// s_waitcnt vmcnt(N) with the other counters left open (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32, int NST = 2>
 __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MB = TM / 32, NB = TN / 32;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(NST == 2 || (AKC && BKC), "deeper pipelines need both operands on the direct path");
   constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes, STAGE = ABYTES + BBYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
-  int tm, tn;
-  tile_coords(p, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int kt_total = p.kt_end[p.nseg - 1];
+  const int M = p.M, N = p.N;
+  const int2 tc = tile_coords(p.tiles_m, p.tiles_n);
+  const int m0 = tc.x * BM, n0 = tc.y * BN;
+  const int kt_end0 = p.kt_end[0], kt_end1 = p.kt_end[1];
   const int kt_lo = blockIdx.y * p.kt_per_split;
-  const int kt_hi = min(kt_lo + p.kt_per_split, kt_total);
+  const int kt_hi = min(kt_lo + p.kt_per_split, p.kt_total);
+  const uint16_t *a0 = p.a[0], *a1 = p.a[1], *a2 = p.a[2];
+  const uint16_t *b0 = p.b[0], *b1 = p.b[1], *b2 = p.b[2];
+  const int64_t lda0 = p.lda[0], lda1 = p.lda[1], lda2 = p.lda[2];
+  const int64_t ldb0 = p.ldb[0], ldb1 = p.ldb[1], ldb2 = p.ldb[2];
+  const int K0 = p.K[0], K1 = p.K[1], K2 = p.K[2];
 
   f32x16 acc[MB][NB];
 #pragma unroll
@@ -218,51 +313,108 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  Loader<BM, NT, AKC> la;
-  Loader<BN, NT, BKC> lb;
-  auto fetch = [&](int kt) {
-    const int s = kt < p.kt_end[0] ? 0 : (kt < p.kt_end[1] ? 1 : 2);
-    const int k0 = (kt - (s ? p.kt_end[s - 1] : 0)) * kBK;
-    la.load(p.a[s], p.lda[s], m0, p.M, k0, p.K[s], tid);
-    lb.load(p.b[s], p.ldb[s], n0, p.N, k0, p.K[s], tid);
+  Copier<BM, NT, AKC> ca;
+  Copier<BN, NT, BKC> cb;
+#define DORA_FETCH(KT, STAGE)                                                              \
+  do {                                                                                     \
+    const int s_ = (KT) < kt_end0 ? 0 : ((KT) < kt_end1 ? 1 : 2);                          \
+    const int k0_ = ((KT) - (s_ == 0 ? 0 : (s_ == 1 ? kt_end0 : kt_end1))) * kBK;          \
+    OpView va_, vb_;                                                                       \
+    va_.p = s_ == 0 ? a0 : (s_ == 1 ? a1 : a2);                                            \
+    va_.ld = s_ == 0 ? lda0 : (s_ == 1 ? lda1 : lda2);                                     \
+    va_.K = s_ == 0 ? K0 : (s_ == 1 ? K1 : K2);                                            \
+    vb_.p = s_ == 0 ? b0 : (s_ == 1 ? b1 : b2);                                            \
+    vb_.ld = s_ == 0 ? ldb0 : (s_ == 1 ? ldb1 : ldb2);                                     \
+    vb_.K = va_.K;                                                                         \
+    ca.issue((STAGE), va_, m0, M, k0_, tid, wave, lane);                                   \
+    cb.issue((STAGE) + ABYTES, vb_, n0, N, k0_, tid, wave, lane);                          \
+  } while (0)
+
+  // One LDS stage: 4 steps of 16 k.  Fragments for step kk+1 are read while
+  // the MFMAs of step kk run (two register sets), so LDS latency hides behind
+  // the matrix cores instead of stalling them.
+  auto mma_stage = [&](const uint8_t* As) {
+    const uint8_t* Bs = As + ABYTES;
+    bf16x8 af[2][MB], bfg[2][NB];
+    auto read = [&](int set, int kk) {
+      const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) af[set][i] = lds_frag(As, wm * TM + i * 32 + (lane & 31), ch);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bfg[set][j] = lds_frag(Bs, wn * TN + j * 32 + (lane & 31), ch);
+    };
+    read(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int cs = kk & 1;
+      if (kk + 1 < kBK / 16) read(cs ^ 1, kk + 1);
+      // keep the reads of step kk+1 ahead of the MFMAs of step kk
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[cs][j], af[cs][i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  if (kt_lo < kt_hi) {
-    fetch(kt_lo);
-    la.store(smem, tid);
-    lb.store(smem + ABYTES, tid);
-    __syncthreads();
-    for (int kt = kt_lo; kt < kt_hi; ++kt) {
-      const int cur = (kt - kt_lo) & 1;
-      const bool more = kt + 1 < kt_hi;
-      if (more) fetch(kt + 1);
-      const uint8_t* As = smem + cur * STAGE;
-      const uint8_t* Bs = As + ABYTES;
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int ch = kk * 2 + (lane >> 5);
-        bf16x8 af[MB], bfg[NB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) af[i] = lds_frag(As, wm * TM + i * 32 + (lane & 31), ch);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) bfg[j] = lds_frag(Bs, wn * TN + j * 32 + (lane & 31), ch);
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
-      }
-      if (more) {
-        uint8_t* nx = smem + (cur ^ 1) * STAGE;
-        la.store(nx, tid);
-        lb.store(nx + ABYTES, tid);
-      }
+  if constexpr (NST == 2) {
+    if (kt_lo < kt_hi) {
+      DORA_FETCH(kt_lo, smem);
+      ca.commit(smem, tid);
+      cb.commit(smem + ABYTES, tid);
+      wait_vmem();
       __syncthreads();
+      for (int kt = kt_lo; kt < kt_hi; ++kt) {
+        const int cur = (kt - kt_lo) & 1;
+        const bool more = kt + 1 < kt_hi;
+        uint8_t* nx = smem + (cur ^ 1) * STAGE;
+        if (more) DORA_FETCH(kt + 1, nx);
+        mma_stage(smem + cur * STAGE);
+        if (more) {
+          ca.commit(nx, tid);
+          cb.commit(nx + ABYTES, tid);
+        }
+        wait_vmem();
+        __syncthreads();
+      }
+    }
+  } else {
+    // NST-stage ring, both operands copied straight to LDS: tile kt+NST-1 is
+    // in flight while tile kt is multiplied.
+    constexpr int kLoads = DmaKC<BM, NT / 64>::kInstr + DmaKC<BN, NT / 64>::kInstr;
+    static_assert(kLoads * (NST - 2) < 64, "outstanding loads exceed vmcnt");
+    if (kt_lo < kt_hi) {
+#pragma unroll
+      for (int i = 0; i < NST - 1; ++i)
+        if (kt_lo + i < kt_hi) DORA_FETCH(kt_lo + i, smem + i * STAGE);
+      wait_vmem();
+      __syncthreads();
+      int cur = 0;
+      for (int kt = kt_lo; kt < kt_hi; ++kt) {
+        const int ahead = kt + NST - 1;
+        int slot = cur + NST - 1;
+        if (slot >= NST) slot -= NST;
+        if (ahead < kt_hi) DORA_FETCH(ahead, smem + slot * STAGE);
+        mma_stage(smem + cur * STAGE);
+        if (ahead < kt_hi)
+          wait_vmem_le<kLoads * (NST - 2)>();   // tile kt+1 has landed
+        else
+          wait_vmem();
+        __syncthreads();
+        cur = cur + 1 == NST ? 0 : cur + 1;
+      }
     }
   }
+#undef DORA_FETCH
 
   // Epilogue.  acc[i][j][v]: m = m0 + wm*TM + i*32 + lane%32,
   //                          n = n0 + wn*TN + j*32 + (v/4)*8 + (lane/32)*4 + v%4.
+  const int64_t ldc = p.ldc;
+  const float alpha = p.alpha;
+  const void* mag = p.mag;
+  const float* nrm = p.norm;
   void* cbase = OUT_F32 ? (void*)(reinterpret_cast<float*>(p.c) + blockIdx.y * p.split_stride)
                         : (void*)(reinterpret_cast<uint16_t*>(p.c) + blockIdx.y * p.split_stride);
 #pragma unroll
@@ -270,20 +422,20 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int n = n0 + wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
-      if (n >= p.N) continue;
+      if (n >= N) continue;
       f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
-      if (EPI == kEpiCompose) gm1 = gm1_4<!OUT_F32>(p, n);
+      if (EPI == kEpiCompose) gm1 = gm1_4<!OUT_F32>(mag, nrm, n);
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int m = m0 + wm * TM + i * 32 + (lane & 31);
-        if (m >= p.M) continue;
+        if (m >= M) continue;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float z = p.alpha * acc[i][j][g * 4 + e];
+          const float z = alpha * acc[i][j][g * 4 + e];
           v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
         }
-        store4<OUT_F32>(p, cbase, m, n, v[0], v[1], v[2], v[3]);
+        store4<OUT_F32>(cbase, ldc, m, n, v[0], v[1], v[2], v[3]);
       }
     }
   }
@@ -296,33 +448,35 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
   __shared__ float As[BKF][BM + 4];
   __shared__ float Bs[BKF][BN + 4];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  int tm, tn;
-  tile_coords(p, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int2 tc = tile_coords(p.tiles_m, p.tiles_n);
+  const int m0 = tc.x * BM, n0 = tc.y * BN;
   float acc[4][4] = {};
-  const int kt_total = p.kt_end[p.nseg - 1];   // in 64-deep units, shared with the bf16 path
+  const int kt_total = p.kt_total;   // in 64-deep units, shared with the bf16 path
   const int kt_lo = blockIdx.y * p.kt_per_split;
   const int kt_hi = min(kt_lo + p.kt_per_split, kt_total);
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
     const int s = kt < p.kt_end[0] ? 0 : (kt < p.kt_end[1] ? 1 : 2);
-    const int kbase = (kt - (s ? p.kt_end[s - 1] : 0)) * kBK;
-    const float* a = reinterpret_cast<const float*>(p.a[s]);
-    const float* b = reinterpret_cast<const float*>(p.b[s]);
+    const int kbase = (kt - (s == 0 ? 0 : (s == 1 ? p.kt_end[0] : p.kt_end[1]))) * kBK;
+    const float* a = reinterpret_cast<const float*>(s == 0 ? p.a[0] : (s == 1 ? p.a[1] : p.a[2]));
+    const float* b = reinterpret_cast<const float*>(s == 0 ? p.b[0] : (s == 1 ? p.b[1] : p.b[2]));
+    const int64_t lda = s == 0 ? p.lda[0] : (s == 1 ? p.lda[1] : p.lda[2]);
+    const int64_t ldb = s == 0 ? p.ldb[0] : (s == 1 ? p.ldb[1] : p.ldb[2]);
+    const int Ks = s == 0 ? p.K[0] : (s == 1 ? p.K[1] : p.K[2]);
     for (int ks = 0; ks < kBK; ks += BKF) {
       const int k0 = kbase + ks;
-      if (k0 >= p.K[s]) break;
+      if (k0 >= Ks) break;
       for (int e = tid; e < BM * BKF; e += 256) {
         const int mm = AKC ? e / BKF : e % BM, kk = AKC ? e % BKF : e / BM;
         const int gm = m0 + mm, gk = k0 + kk;
         float va = 0.f;
-        if (gm < p.M && gk < p.K[s])
-          va = AKC ? a[(int64_t)gm * p.lda[s] + gk] : a[(int64_t)gk * p.lda[s] + gm];
+        if (gm < p.M && gk < Ks)
+          va = AKC ? a[(int64_t)gm * lda + gk] : a[(int64_t)gk * lda + gm];
         As[kk][mm] = va;
         const int nn = BKC ? e / BKF : e % BN, kb = BKC ? e % BKF : e / BN;
         const int gn = n0 + nn, gk2 = k0 + kb;
         float vb = 0.f;
-        if (gn < p.N && gk2 < p.K[s])
-          vb = BKC ? b[(int64_t)gn * p.ldb[s] + gk2] : b[(int64_t)gk2 * p.ldb[s] + gn];
+        if (gn < p.N && gk2 < Ks)
+          vb = BKC ? b[(int64_t)gn * ldb + gk2] : b[(int64_t)gk2 * ldb + gn];
         Bs[kb][nn] = vb;
       }
       __syncthreads();
@@ -345,7 +499,7 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
   const int n = n0 + tx * 4;
   if (n >= p.N) return;
   f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
-  if (EPI == kEpiCompose) gm1 = gm1_4<false>(p, n);
+  if (EPI == kEpiCompose) gm1 = gm1_4<false>(p.mag, p.norm, n);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty * 4 + i;
@@ -356,7 +510,7 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
       const float z = p.alpha * acc[i][e];
       v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
     }
-    store4<true>(p, c, m, n, v[0], v[1], v[2], v[3]);
+    store4<true>(c, p.ldc, m, n, v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -392,28 +546,30 @@ constexpr Cfg kCfgs[] = {
     {128, 256, 2, 2},   // 3: 4 waves, 64x128 per wave
     {64, 64, 2, 2},     // 4: 4 waves, 32x32 per wave
     {256, 128, 4, 2},   // 5: 8 waves, 64x64 per wave
+    {256, 256, 2, 2},   // 6: 4 waves, 128x128 per wave
+    {256, 128, 4, 2},   // 7: as 5 with a 3-stage ring (K-contiguous operands only)
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC>
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int NST = 2>
 hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStream_t st) {
   const dim3 block(WM * WN * 64);
   if (out_f32) {
-    hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, true>), grid, block, 0,
-                       st, a);
+    hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, true, NST>), grid,
+                       block, 0, st, a);
     return hipGetLastError();
   }
   if constexpr (AKC && BKC) {   // the compose epilogue belongs to the forward (K-contiguous) GEMM
     if (epi == kEpiCompose) {
-      hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiCompose, false>), grid,
+      hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiCompose, false, NST>), grid,
                          block, 0, st, a);
       return hipGetLastError();
     }
   } else {
     if (epi != kEpiStore) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, false>), grid, block, 0,
-                     st, a);
+  hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, false, NST>), grid,
+                     block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -435,6 +591,10 @@ hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool
     case 3: return launch_layout<128, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 4: return launch_layout<64, 64, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 5: return launch_layout<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 6: return launch_layout<256, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 7:
+      if (!(akc && bkc)) return hipErrorInvalidValue;
+      return launch_bf16<256, 128, 4, 2, true, true, 3>(a, epi, out_f32, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -474,6 +634,7 @@ int fill_args(const GemmProblem& p, KArgs& a) {
   }
   for (int s = ns; s < 3; ++s) a.kt_end[s] = kt;
   a.nseg = ns;
+  a.kt_total = kt;
   a.c = p.c;
   a.ldc = p.ldc;
   a.split_stride = p.split_stride;
@@ -496,24 +657,28 @@ hipError_t run(int cfg, int split, const GemmProblem& p, KArgs& a, int kt, hipSt
 
 }  // namespace
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bkc) {
   if (dtype == kF32 || M <= 0 || N <= 0) return {-1, 1};
   const int64_t ktiles = cdiv64(K, kBK);
   auto tiles = [&](int cfg) { return cdiv64(M, kCfgs[cfg].bm) * cdiv64(N, kCfgs[cfg].bn); };
   // Large outputs: 256 x 256 tiles (8 waves), then 256 x 128 (8 waves).
   if (tiles(0) >= 256) return {0, 1};
   if (tiles(5) >= 200) return {5, 1};
-  // Skinny or small: 128 x 128 tiles, split along K to ~384 workgroups
-  // (measured best for the N = r projections of the d = 8192, r = 384 layer).
-  const int64_t t = tiles(2);
-  int64_t split = (384 + t / 2) / t;
+  // Skinny or small, split along K.  Measured on the d = 8192, r = 384 layer:
+  // K-contiguous pairs do best on 128 x 128 tiles at ~384 workgroups, pairs
+  // with a transposed operand on 256 x 256 tiles at ~256 workgroups.
+  const bool direct = akc && bkc;
+  const int cfg = direct ? 2 : 0;
+  const int64_t target = direct ? 384 : 256;
+  const int64_t t = tiles(cfg);
+  int64_t split = (target + t / 2) / t;
   split = std::min<int64_t>(split, std::max<int64_t>(1, ktiles / 8));
   split = std::max<int64_t>(1, std::min<int64_t>(split, 16));
-  return {2, (int)split};
+  return {cfg, (int)split};
 }
 
-size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype) {
-  const GemmPlan pl = plan_gemm(M, N, K, dtype);
+size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bkc) {
+  const GemmPlan pl = plan_gemm(M, N, K, dtype, akc, bkc);
   return pl.split > 1 ? (size_t)pl.split * M * N * 4 : 0;
 }
 
@@ -538,12 +703,12 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
   }
 
   int cfg = p.cfg;
-  if (cfg < 0 || cfg >= kNumCfgs) cfg = plan_gemm(p.M, p.N, K, dtype).cfg;
+  if (cfg < 0 || cfg >= kNumCfgs) cfg = plan_gemm(p.M, p.N, K, dtype, p.a_kcontig, p.b_kcontig).cfg;
   if (p.split > 1 || p.out_f32) {   // caller-managed partial sums (or a plain float32 output)
     LaunchTimer timer(label, st);
     return run(cfg, p.split < 1 ? 1 : p.split, p, a, kt, st, p.out_f32);
   }
-  GemmPlan pl = plan_gemm(p.M, p.N, K, dtype);
+  GemmPlan pl = plan_gemm(p.M, p.N, K, dtype, p.a_kcontig, p.b_kcontig);
   if (p.cfg >= 0) pl.cfg = cfg;
   if (p.force_split > 0) pl.split = p.force_split;
   const size_t need = (size_t)pl.split * p.M * p.N * 4;

@@ -49,17 +49,19 @@ struct GemmPlan {
   int split;   // split-K factor
 };
 
-// Tile configuration and split-K factor for a layer-dtype GEMM of this size.
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype);
+// Tile configuration and split-K factor for a layer-dtype GEMM of this size
+// and operand layout.
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc = true, bool bkc = true);
 
-// Scratch bytes the split-K path of gemm() needs for this size (0 if unsplit).
-size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype);
+// Scratch bytes the split-K path of gemm() needs for this problem (0 if unsplit).
+size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype, bool akc = true,
+                          bool bkc = true);
 
 // Enqueue C = sum over segments; picks the tile configuration from the shape.
 hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* label);
 
 
-// G partial sums -> (s/2) * G, symmetrised; bf16: written as hi + lo bf16 pair.
+// G partial sums -> (s/2) * G; bf16: written as a hi + lo bf16 pair.
 hipError_t gram_finalize(const float* part, int splits, int64_t r, float s, int dtype,
                          void* g_hi, void* g_lo, hipStream_t st);
 

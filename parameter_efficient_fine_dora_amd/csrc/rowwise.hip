@@ -54,23 +54,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---- Gram finisher ------------------------------------------------------------
-// part[z][j][l], z < splits: split-K partial sums of G = A A^T.  Writes
-// (s/2) * G, symmetrised as (G[j][l] + G[l][j]) / 2 so that B (s/2 G)^T is
-// exactly B (s/2 G).  bf16 layers get it as a hi + lo bf16 pair (hi = round(v),
-// lo = round(v - hi)), which keeps ~16 significant bits through the bf16 MFMA.
+// part[z], z < splits: split-K partial sums of G = A A^T, added in a fixed
+// order.  Writes (s/2) G; bf16 layers get it as a hi + lo bf16 pair
+// (hi = round(v), lo = round(v - hi)), which keeps ~16 significant bits through
+// the bf16 MFMA.  G is symmetric (up to the rounding of its partial sums), so
+// the projection may use its rows for its columns.
 __global__ __launch_bounds__(256) void dora_gram_finalize(const float* part, int splits,
-                                                          int64_t r, float quarter_s, int bf,
+                                                          int64_t rr, float half_s, int bf,
                                                           void* g_hi, void* g_lo) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= r * r) return;
-  const int64_t j = idx / r, l = idx - j * r;
-  const int64_t rr = r * r;
-  float a = 0.f, b = 0.f;
-  for (int z = 0; z < splits; ++z) {
-    a += part[z * rr + j * r + l];
-    b += part[z * rr + l * r + j];
-  }
-  const float v = quarter_s * (a + b);
+  if (idx >= rr) return;
+  float a = 0.f;
+  for (int z = 0; z < splits; ++z) a += part[z * rr + idx];
+  const float v = half_s * a;
   if (bf) {
     const uint16_t hi = f32_to_bf16(v);
     const float rest = v - bf16_to_f32(hi);
@@ -164,7 +160,25 @@ __global__ __launch_bounds__(256) void dora_compose_fwd(void* y, const void* slo
   }
   const int64_t t0 = (int64_t)blockIdx.y * tok_per_block;
   const int64_t t1 = min(T, t0 + tok_per_block);
-  for (int64_t t = t0; t < t1; ++t) {
+  constexpr int U = 4;   // tokens in flight per thread
+  int64_t t = t0;
+  for (; t + U <= t1; t += U) {
+    float base[U][V::kN], lo[U][V::kN];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      V::load(y, (t + u) * nvec + cv, base[u]);
+      V::load(slora, (t + u) * nvec + cv, lo[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float out[V::kN];
+#pragma unroll
+      for (int q = 0; q < V::kN; ++q)
+        out[q] = base[u][q] + fmaf(gm1[q], base[u][q], g[q] * lo[u][q]);
+      V::store(y, (t + u) * nvec + cv, out);
+    }
+  }
+  for (; t < t1; ++t) {
     float base[V::kN], lo[V::kN], out[V::kN];
     V::load(y, t * nvec + cv, base);
     V::load(slora, t * nvec + cv, lo);
@@ -198,7 +212,27 @@ __global__ __launch_bounds__(256) void dora_compose_bwd(const void* gy, const vo
   }
   const int64_t t0 = (int64_t)blockIdx.y * tok_per_block;
   const int64_t t1 = min(T, t0 + tok_per_block);
-  for (int64_t t = t0; t < t1; ++t) {
+  constexpr int U = 4;   // tokens in flight per thread
+  int64_t t = t0;
+  for (; t + U <= t1; t += U) {
+    float a[U][V::kN], b[U][V::kN];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      V::load(gy, (t + u) * nvec + cv, a[u]);
+      V::load(y, (t + u) * nvec + cv, b[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float o[V::kN];
+#pragma unroll
+      for (int q = 0; q < V::kN; ++q) {
+        o[q] = g[q] * a[u][q];
+        acc[q] = fmaf(a[u][q], b[u][q], acc[q]);
+      }
+      V::store(gz, (t + u) * nvec + cv, o);
+    }
+  }
+  for (; t < t1; ++t) {
     float a[V::kN], b[V::kN], o[V::kN];
     V::load(gy, t * nvec + cv, a);
     V::load(y, t * nvec + cv, b);
@@ -215,14 +249,21 @@ __global__ __launch_bounds__(256) void dora_compose_bwd(const void* gy, const vo
     *reinterpret_cast<f32x4*>(dst + q) = f32x4{acc[q], acc[q + 1], acc[q + 2], acc[q + 3]};
 }
 
+// 64 columns per workgroup, the partial blocks split over 4 thread rows and
+// combined through LDS in a fixed order.
 template <bool BF>
 __global__ __launch_bounds__(256) void dora_dm_finalize(const float* dm_part, int64_t blocks,
                                                         const void* m, float* dm, int64_t d_out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= d_out) return;
+  __shared__ float red[4][64];
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + c;
   float s = 0.f;
-  for (int64_t b = 0; b < blocks; ++b) s += dm_part[b * d_out + i];
-  dm[i] = s / Vec<BF>::scalar(m, i);
+  if (i < d_out)
+    for (int64_t b = q; b < blocks; b += 4) s += dm_part[b * d_out + i];
+  red[q][c] = s;
+  __syncthreads();
+  if (q == 0 && i < d_out)
+    dm[i] = ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) / Vec<BF>::scalar(m, i);
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -234,7 +275,7 @@ hipError_t gram_finalize(const float* part, int splits, int64_t r, float s, int 
   if (r <= 0) return hipSuccess;
   LaunchTimer t("gram_finalize", st);
   hipLaunchKernelGGL(dora_gram_finalize, dim3((unsigned)cdiv(r * r, 256)), dim3(256), 0, st, part,
-                     splits, r, 0.25f * s, dtype == kBF16 ? 1 : 0, g_hi, g_lo);
+                     splits, r * r, 0.5f * s, dtype == kBF16 ? 1 : 0, g_hi, g_lo);
   return hipGetLastError();
 }
 
@@ -288,7 +329,7 @@ hipError_t compose_bwd(const void* gy, const void* y, const void* m, const float
 hipError_t dm_finalize(const float* dm_part, int64_t blocks, const void* m, float* dm,
                        int64_t d_out, int dtype, hipStream_t st) {
   LaunchTimer t("dm_finalize", st);
-  const dim3 grid((unsigned)cdiv(d_out, 256));
+  const dim3 grid((unsigned)cdiv(d_out, 64));
   if (dtype == kBF16)
     hipLaunchKernelGGL(dora_dm_finalize<true>, grid, dim3(256), 0, st, dm_part, blocks, m, dm,
                        d_out);
