@@ -19,6 +19,7 @@ times the float64 oracle (dense W0 + sBA) on the host for one full step.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +32,34 @@ if ROOT not in sys.path:
 METRIC = "DoRA layer fwd+bwd µs & norm/compose GB/s (% HBM peak), d=8192 r=384 bf16"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFS = 2500.0         # MI355X dense bf16 MFMA, TFLOP/s
+
+
+KERNEL_SOURCES = ["include/dora.h"] + [
+    f"parameter_efficient_fine_dora_amd/csrc/{f}"
+    for f in ("api.hip", "gemm.hip", "rowwise.hip", "common.h", "kernels.h")]
+WORKLOAD_TAG = "highrank_d8192_r384_t4096"
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the library sources: recorded counter data applies only to this build."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """Per-kernel HBM bytes from the committed PMC summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD_TAG}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return {}
+    return rec.get("traffic", {})
 
 
 def algorithmic_work(d_out, d_in, r, T):
@@ -59,7 +88,7 @@ def algorithmic_work(d_out, d_in, r, T):
     }
 
 
-def kernel_table(timing, steps, work):
+def kernel_table(timing, steps, work, traffic):
     out = {}
     for name, (count, total_ms) in sorted(timing.items(), key=lambda kv: -kv[1][1]):
         per = count / steps if steps else 0
@@ -74,6 +103,8 @@ def kernel_table(timing, steps, work):
             else:
                 gbs = amount / (avg_us * 1e-6) / 1e9
                 row.update(gbps=round(gbs, 1), frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+        if name in traffic:
+            row["hbm_traffic_bytes"] = traffic[name]["total_bytes"]
         out[name] = row
     tot = sum(v[1] for v in timing.values())
     for name, row in out.items():
@@ -189,19 +220,22 @@ def main():
     ops.timing_enable(False)
     timing = ops.timing_collect()
     work = algorithmic_work(d_out, d_in, r, T)
-    kernels = kernel_table(timing, args.steps, work)
+    traffic = recorded_traffic() if not flags else {}
+    kernels = kernel_table(timing, args.steps, work, traffic)
     dominant = max(timing, key=lambda k: timing[k][1])
     kind, amount = work[dominant]
     avg_s = timing[dominant][1] / timing[dominant][0] * 1e-3
     if kind == "flop":
         achieved = amount / avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFS, 4),
+                "traffic": traffic.get(dominant, {}).get("total_bytes"),
                 "kernel": dominant, "per_launch": f"{amount / 1e9:.1f} GFLOP"}
     else:
         achieved = amount / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic.get(dominant, {}).get("total_bytes"),
                 "kernel": dominant, "per_launch": f"{amount / 1e6:.1f} MB"}
 
     cpu = None
@@ -220,6 +254,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "kernel_source_hash": kernel_source_hash(),
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(rec))

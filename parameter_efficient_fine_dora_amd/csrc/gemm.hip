@@ -82,56 +82,45 @@ struct OpView {
 // K-contiguous operand, R rows x 64 k, copied straight into LDS with
 // buffer_load ... lds: one wave instruction fills 8 rows x 128 B, lane l
 // takes row l/8 and physical chunk l%8, i.e. logical chunk (l%8) ^ swz(row).
+// Per-lane byte offsets are fixed for a K segment and computed once
+// (prepare); each 64-deep step only moves the scalar buffer base (issue).
 template <int R, int NW>
 struct DmaKC {
   static constexpr int kInstr = R / 8 / NW;   // per wave
   static_assert(R % (8 * NW) == 0, "rows must split evenly over the waves");
-  __device__ __forceinline__ static void issue(uint8_t* lds_tile, const OpView& v, int row0,
-                                               int nrows, int k0, int wave, int lane) {
-    int64_t rows = nrows - row0;
+  const uint16_t* base;   // operand rows of this tile, k = 0
+  int64_t ld;
+  int64_t rows;           // valid rows in the tile
+  int K;
+  uint32_t off[kInstr];   // row * ld * 2 + chunk * 16
+  uint32_t kcol[kInstr];  // chunk * 8 (k offset of the lane's 16 bytes)
+  __device__ __forceinline__ void prepare(const OpView& v, int row0, int nrows, int wave,
+                                          int lane) {
+    rows = nrows - row0;
     if (rows > R) rows = R;
-    const Rsrc rs = make_rsrc(v.p + (int64_t)row0 * v.ld, rows * v.ld * 2);
+    base = v.p + (int64_t)row0 * v.ld;
+    ld = v.ld;
+    K = v.K;
+#pragma unroll
+    for (int i = 0; i < kInstr; ++i) {
+      const int row = (wave * kInstr + i) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(row);
+      kcol[i] = (uint32_t)kc * 8u;
+      // 32-bit arithmetic: a tile spans < 2^31 bytes (the library limits every dimension)
+      off[i] = (uint32_t)row * (uint32_t)(v.ld * 2) + kcol[i] * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(uint8_t* lds_tile, int k0, int wave) const {
+    // rebased at column k0: rows past the tile's valid ones fall beyond the records
+    const Rsrc rs = make_rsrc(base + k0, rows * ld * 2 - (int64_t)k0 * 2);
+    const bool tail = k0 + kBK > K;   // uniform; only a segment's last step can be partial
 #pragma unroll
     for (int i = 0; i < kInstr; ++i) {
       const int rbase = (wave * kInstr + i) * 8;
-      const int row = rbase + (lane >> 3);
-      const int kc = (lane & 7) ^ swz(row);
-      const int gk = k0 + kc * 8;
-      // 32-bit arithmetic: a tile spans < 2^31 bytes (the library limits every dimension)
-      const uint32_t off = gk < v.K ? (uint32_t)row * (uint32_t)(v.ld * 2) + (uint32_t)gk * 2u : kOob;
+      const uint32_t o = (tail && (int)kcol[i] + k0 >= K) ? kOob : off[i];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(lds_tile + rbase * kRowBytes), 16, (int)off,
+          rs, (__attribute__((address_space(3))) void*)(lds_tile + rbase * kRowBytes), 16, (int)o,
           0, 0, 0);
-    }
-  }
-};
-
-// K-contiguous operand through registers: one 16-byte chunk (8 k) per copy.
-template <int R, int NT>
-struct RegKC {
-  static constexpr int kChunks = R * 8;
-  static constexpr int kPer = (kChunks + NT - 1) / NT;
-  u32x4 v[kPer];
-  __device__ __forceinline__ void load(const OpView& o, int row0, int nrows, int k0, int tid) {
-    int64_t rows = nrows - row0;
-    if (rows > R) rows = R;
-    const Rsrc rs = make_rsrc(o.p + (int64_t)row0 * o.ld, rows * o.ld * 2);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * NT;
-      const int row = c >> 3, kc = c & 7;
-      const int gk = k0 + kc * 8;
-      const bool ok = (kChunks % NT == 0 || c < kChunks) && gk < o.K;
-      v[i] = bload16(rs, ok ? (uint32_t)row * (uint32_t)(o.ld * 2) + (uint32_t)gk * 2u : kOob);
-    }
-  }
-  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * NT;
-      if (kChunks % NT != 0 && c >= kChunks) continue;
-      const int row = c >> 3, kc = c & 7;
-      *reinterpret_cast<u32x4*>(lds + row * kRowBytes + ((kc ^ swz(row)) << 4)) = v[i];
     }
   }
 };
@@ -156,11 +145,22 @@ struct RegMC {
     rc = (rest % kHi) * 8 + lo;
     kq = (rest / kHi) * 2 + kh;
   }
-  __device__ __forceinline__ void load(const OpView& o, int row0, int nrows, int k0, int tid) {
-    int64_t krows = o.K - k0;
+  const uint16_t* base;    // column row0 of the operand, k = 0
+  int64_t ld;
+  int K, row0, nrows;
+  __device__ __forceinline__ void prepare(const OpView& o, int r0, int nr, int) {
+    base = o.p + r0;
+    ld = o.ld;
+    K = o.K;
+    row0 = r0;
+    nrows = nr;
+  }
+  __device__ __forceinline__ void load(int k0, int tid) {
+    int64_t krows = K - k0;
     if (krows > kBK) krows = kBK;
-    // rebased at (k0, row0); rows k >= K fall past the end of the records
-    const Rsrc rs = make_rsrc(o.p + (int64_t)k0 * o.ld + row0, krows * o.ld * 2 - (int64_t)row0 * 2);
+    // rebased at row k0; rows k >= K fall past the end of the records
+    const Rsrc rs = make_rsrc(base + (int64_t)k0 * ld, krows * ld * 2 - (int64_t)row0 * 2);
+    const uint32_t ld2 = (uint32_t)(ld * 2);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int b = tid + i * NT;
@@ -168,10 +168,8 @@ struct RegMC {
       block_of(b, kq, rc);
       const bool ok = (kBlocks % NT == 0 || b < kBlocks) && row0 + rc * 8 < nrows;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kl = kq * 4 + j;
-        v[i][j] = bload16(rs, ok ? (uint32_t)kl * (uint32_t)(o.ld * 2) + (uint32_t)rc * 16u : kOob);
-      }
+      for (int j = 0; j < 4; ++j)
+        v[i][j] = bload16(rs, ok ? (uint32_t)(kq * 4 + j) * ld2 + (uint32_t)rc * 16u : kOob);
     }
   }
   __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
@@ -208,21 +206,24 @@ template <int R, int NT, bool KC>
 struct Copier;
 template <int R, int NT>
 struct Copier<R, NT, true> {
-  static constexpr bool kDirect = true;
-  __device__ __forceinline__ void issue(uint8_t* lds, const OpView& o, int row0, int nrows, int k0,
-                                        int tid, int wave, int lane) {
-    DmaKC<R, NT / 64>::issue(lds, o, row0, nrows, k0, wave, lane);
+  DmaKC<R, NT / 64> d;
+  __device__ __forceinline__ void prepare(const OpView& o, int row0, int nrows, int tid, int wave,
+                                          int lane) {
+    d.prepare(o, row0, nrows, wave, lane);
+  }
+  __device__ __forceinline__ void issue(uint8_t* lds, int k0, int tid, int wave) {
+    d.issue(lds, k0, wave);
   }
   __device__ __forceinline__ void commit(uint8_t*, int) {}
 };
 template <int R, int NT>
 struct Copier<R, NT, false> {
-  static constexpr bool kDirect = false;
   RegMC<R, NT> r;
-  __device__ __forceinline__ void issue(uint8_t*, const OpView& o, int row0, int nrows, int k0,
-                                        int tid, int, int) {
-    r.load(o, row0, nrows, k0, tid);
+  __device__ __forceinline__ void prepare(const OpView& o, int row0, int nrows, int tid, int,
+                                          int) {
+    r.prepare(o, row0, nrows, tid);
   }
+  __device__ __forceinline__ void issue(uint8_t*, int k0, int tid, int) { r.load(k0, tid); }
   __device__ __forceinline__ void commit(uint8_t* lds, int tid) { r.store(lds, tid); }
 };
 
@@ -230,13 +231,14 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* lds, int row, int chun
   return *reinterpret_cast<const bf16x8*>(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4));
 }
 
-// Tile index -> (tile_m, tile_n), XCD-grouped, 4 tile-rows per group.
+// Tile index -> (tile_m, tile_n), XCD-grouped, 8 tile-rows per group (an XCD's
+// 32 CUs then hold an ~8 x 4 block of tiles and share its operand panels in L2).
 // Returns tile_m in .x and tile_n in .y.
 __device__ __forceinline__ int2 tile_coords(int tiles_m, int tiles_n) {
   int L = blockIdx.x;
   const int nwg = gridDim.x;
   if ((nwg & 7) == 0) L = (L & 7) * (nwg >> 3) + (L >> 3);
-  constexpr int kGroup = 4;
+  constexpr int kGroup = 8;
   const int per_group = kGroup * tiles_n;
   const int g = L / per_group;
   const int first = g * kGroup;
@@ -288,7 +290,12 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(NST == 2 || (AKC && BKC), "deeper pipelines need both operands on the direct path");
   constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes, STAGE = ABYTES + BBYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
+  // bf16 outputs leave through LDS: each wave stages its TM x TN tile with rows
+  // padded by 8 elements (conflict-free 8-byte writes, 16-byte aligned reads)
+  constexpr int kStageLd = TN + 8;
+  constexpr int kOutBytes = OUT_F32 ? 0 : WM * WN * TM * kStageLd * 2;
+  constexpr int kSmem = NST * STAGE > kOutBytes ? NST * STAGE : kOutBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -315,19 +322,25 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
 
   Copier<BM, NT, AKC> ca;
   Copier<BN, NT, BKC> cb;
+  int prep_seg = -1;   // K segment the copiers are prepared for
 #define DORA_FETCH(KT, STAGE)                                                              \
   do {                                                                                     \
     const int s_ = (KT) < kt_end0 ? 0 : ((KT) < kt_end1 ? 1 : 2);                          \
     const int k0_ = ((KT) - (s_ == 0 ? 0 : (s_ == 1 ? kt_end0 : kt_end1))) * kBK;          \
-    OpView va_, vb_;                                                                       \
-    va_.p = s_ == 0 ? a0 : (s_ == 1 ? a1 : a2);                                            \
-    va_.ld = s_ == 0 ? lda0 : (s_ == 1 ? lda1 : lda2);                                     \
-    va_.K = s_ == 0 ? K0 : (s_ == 1 ? K1 : K2);                                            \
-    vb_.p = s_ == 0 ? b0 : (s_ == 1 ? b1 : b2);                                            \
-    vb_.ld = s_ == 0 ? ldb0 : (s_ == 1 ? ldb1 : ldb2);                                     \
-    vb_.K = va_.K;                                                                         \
-    ca.issue((STAGE), va_, m0, M, k0_, tid, wave, lane);                                   \
-    cb.issue((STAGE) + ABYTES, vb_, n0, N, k0_, tid, wave, lane);                          \
+    if (s_ != prep_seg) {                                                                  \
+      prep_seg = s_;                                                                       \
+      OpView va_, vb_;                                                                     \
+      va_.p = s_ == 0 ? a0 : (s_ == 1 ? a1 : a2);                                          \
+      va_.ld = s_ == 0 ? lda0 : (s_ == 1 ? lda1 : lda2);                                   \
+      va_.K = s_ == 0 ? K0 : (s_ == 1 ? K1 : K2);                                          \
+      vb_.p = s_ == 0 ? b0 : (s_ == 1 ? b1 : b2);                                          \
+      vb_.ld = s_ == 0 ? ldb0 : (s_ == 1 ? ldb1 : ldb2);                                   \
+      vb_.K = va_.K;                                                                       \
+      ca.prepare(va_, m0, M, tid, wave, lane);                                             \
+      cb.prepare(vb_, n0, N, tid, wave, lane);                                             \
+    }                                                                                      \
+    ca.issue((STAGE), k0_, tid, wave);                                                     \
+    cb.issue((STAGE) + ABYTES, k0_, tid, wave);                                            \
   } while (0)
 
   // One LDS stage: 4 steps of 16 k.  Fragments for step kk+1 are read while
@@ -417,6 +430,43 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   const float* nrm = p.norm;
   void* cbase = OUT_F32 ? (void*)(reinterpret_cast<float*>(p.c) + blockIdx.y * p.split_stride)
                         : (void*)(reinterpret_cast<uint16_t*>(p.c) + blockIdx.y * p.split_stride);
+  if constexpr (!OUT_F32) {
+    // Stage the wave's tile in LDS (the K loop ended on a barrier, so every
+    // stage is free), then write whole 16-byte pieces of contiguous rows.
+    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * TM * kStageLd;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int nl = j * 32 + g * 8 + (lane >> 5) * 4;
+        const int n = n0 + wn * TN + nl;
+        f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
+        if (EPI == kEpiCompose && n < N) gm1 = gm1_4<true>(mag, nrm, n);
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int ml = i * 32 + (lane & 31);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float z = alpha * acc[i][j][g * 4 + e];
+            v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
+          }
+          *reinterpret_cast<u32x2*>(stg + ml * kStageLd + nl) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      }
+    }
+    constexpr int kChunksPerRow = TN / 8;
+#pragma unroll 4
+    for (int c = lane; c < TM * kChunksPerRow; c += 64) {
+      const int row = c / kChunksPerRow, ch = c - row * kChunksPerRow;
+      const int m = m0 + wm * TM + row, n = n0 + wn * TN + ch * 8;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stg + row * kStageLd + ch * 8);
+      if (m < M && n < N)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(cbase) + (int64_t)m * ldc + n) = val;
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
 #pragma unroll
@@ -546,8 +596,6 @@ constexpr Cfg kCfgs[] = {
     {128, 256, 2, 2},   // 3: 4 waves, 64x128 per wave
     {64, 64, 2, 2},     // 4: 4 waves, 32x32 per wave
     {256, 128, 4, 2},   // 5: 8 waves, 64x64 per wave
-    {256, 256, 2, 2},   // 6: 4 waves, 128x128 per wave
-    {256, 128, 4, 2},   // 7: as 5 with a 3-stage ring (K-contiguous operands only)
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -591,10 +639,7 @@ hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool
     case 3: return launch_layout<128, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 4: return launch_layout<64, 64, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 5: return launch_layout<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 6: return launch_layout<256, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 7:
-      if (!(akc && bkc)) return hipErrorInvalidValue;
-      return launch_bf16<256, 128, 4, 2, true, true, 3>(a, epi, out_f32, grid, st);
+
     default: return hipErrorInvalidValue;
   }
 }
