@@ -38,10 +38,9 @@
  *              negative = DORA_ERR_* below.  DORA_ERR_HIP means the HIP runtime
  *              rejected a launch (hipGetLastError is checked after each one);
  *              kernels already enqueued may then have run.
- *   Sizes      d_out, d_in >= 1; r >= 0; tokens >= 0.  d_out, d_in and r must
- *              be multiples of 8 (16-byte rows for both dtypes).  Every
- *              element count must stay below 2^31 per tensor row-block and
- *              2^62 in total.
+ *   Sizes      1 <= d_out, d_in < 2^22; 0 <= r < 2^22; 0 <= tokens < 2^31.
+ *              d_out, d_in and r must be multiples of 8 (16-byte rows for both
+ *              dtypes).
  */
 #ifndef DORA_H
 #define DORA_H
@@ -70,7 +69,7 @@ typedef struct {
 } dora_shape;
 
 /* flags */
-#define DORA_FLAG_EXACT_NORM_GRAD   (1u << 0)  /* backward: undetached norm gradient (DoRA reading notes, Appendix A.1) */
+#define DORA_FLAG_EXACT_NORM_GRAD   (1u << 0)  /* backward: undetached norm gradient (DoRA reading notes, Appendix A.1); needs the matching workspace size */
 #define DORA_FLAG_SEPARATE_COMPOSE  (1u << 1)  /* forward/backward: run the standalone compose kernels instead of the GEMM-fused ones */
 
 /* op ids for dora_workspace_bytes */
@@ -130,8 +129,13 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
  *   grad_x   = gz W0 + s (gz B) A
  *   grad_B   = s gz^T (x A^T)      = gz^T xs
  *   grad_A   = s (gz B)^T x
- * W0 receives no gradient (it is frozen).  DORA_FLAG_EXACT_NORM_GRAD is not
- * implemented in this version and returns DORA_ERR_FLAGS.
+ * With DORA_FLAG_EXACT_NORM_GRAD the norm is not detached: dV'_i is projected
+ * off V'_i (Appendix A.1 of the notes), which adds, with
+ * k'_i = -s m_i grad_m_i / n_i^2 and Bk' = diag(k') B,
+ *   grad_B += diag(k') (W0 A^T + s B A A^T)
+ *   grad_A += Bk'^T W0 + s (Bk'^T B) A
+ * (grad_x and grad_m are the same in both modes).  W0 receives no gradient
+ * (it is frozen).
  *   grad_y, x, W0, A, B, m, norm, y   inputs (norm and y as written by
  *                                     dora_forward for the same layer)
  *   xs        s * (x A^T) as written by dora_forward, or NULL to recompute it

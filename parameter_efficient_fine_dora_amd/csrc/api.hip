@@ -54,10 +54,16 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 size_t esize(int dtype) { return dtype == kBF16 ? 2 : 4; }
 
+// Every row stride the kernels see is d_out, d_in or r; keeping them below
+// 2^22 keeps a 256-row tile's byte offsets inside the 31 bits the buffer
+// loads use.  Tokens only count rows and may reach 2^31 - 1.
+constexpr int64_t kMaxFeature = int64_t(1) << 22;
+
 bool shape_ok(const dora_shape& s) {
   const int64_t lim = int64_t(1) << 31;
   if (s.d_out < 1 || s.d_in < 1 || s.r < 0 || s.tokens < 0) return false;
-  if (s.d_out >= lim || s.d_in >= lim || s.r >= lim || s.tokens >= lim) return false;
+  if (s.d_out >= kMaxFeature || s.d_in >= kMaxFeature || s.r >= kMaxFeature || s.tokens >= lim)
+    return false;
   if (s.d_out % 8 || s.d_in % 8 || s.r % 8) return false;
   const double cap = 4.0e18;
   if ((double)s.d_out * s.d_in > cap || (double)s.tokens * s.d_out > cap ||
@@ -80,6 +86,10 @@ struct Layout {
   size_t gpart = 0, ghi = 0, glo = 0, P = 0;     // norm
   size_t xs = 0, slora = 0;                      // forward
   size_t gz = 0, ts = 0, dmpart = 0;             // backward
+  // backward with the undetached norm gradient
+  size_t dm = 0, kappa = 0, bk = 0, egpart = 0, eghi = 0, eglo = 0, q = 0, hpart = 0, hmat = 0,
+         hlo = 0, d1 = 0;
+  int qsplits = 1, hsplits = 1, d1splits = 1;
   size_t scratch = 0, scratch_bytes = 0;         // split-K partial sums
   size_t total = 0;
   int splits = 1, psplits = 1;
@@ -129,6 +139,24 @@ Layout layout(const dora_shape& s, int op) {
     need(s.tokens, s.d_in, s.d_out + s.r, true, false);  // dx
     need(s.d_out, s.r, s.tokens, false, false);          // dB
     need(s.r, s.d_in, s.tokens, false, false);           // dA
+    if ((s.flags & DORA_FLAG_EXACT_NORM_GRAD) && s.r > 0) {
+      L.dm = take((size_t)s.d_out * 4);
+      L.kappa = take((size_t)s.d_out * 4);
+      L.bk = take((size_t)s.d_out * r * e);
+      L.splits = gram_splits(s);
+      L.egpart = take((size_t)L.splits * r * r * 4);
+      L.eghi = take(r * r * (s.dtype == kBF16 ? 2 : 4));
+      L.eglo = take(s.dtype == kBF16 ? r * r * 2 : 0);
+      L.qsplits = p_splits(s);
+      L.q = take((size_t)L.qsplits * s.d_out * r * 4);
+      L.hsplits = plan_gemm(s.r, s.r, s.d_out, dt, false, false).split;
+      L.hpart = take((size_t)L.hsplits * r * r * 4);
+      L.hmat = take(r * r * e);
+      L.hlo = take(r * r * 2);
+      L.d1splits = plan_gemm(s.d_out, s.r, s.tokens, dt, false, false).split;
+      L.d1 = take((size_t)L.d1splits * s.d_out * r * 4);
+      need(s.r, s.d_in, s.tokens + s.d_out + s.r, false, false);   // dA with the A.1 terms
+    }
   }
   L.scratch = take(scratch);
   L.scratch_bytes = scratch;
@@ -199,7 +227,7 @@ int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, 
     g.split_stride = s.r * s.r;
     g.cfg = plan_gemm(s.r, s.r, s.d_in, dt).cfg;
     HIP_TRY(gemm(g, dt, st, "gram_AAt"));
-    HIP_TRY(gram_finalize(gpart, L.splits, s.r, s.s, dt, ghi, glo, st));
+    HIP_TRY(gram_finalize(gpart, L.splits, s.r, 0.5f * s.s, dt, ghi, glo, st, "gram_finalize"));
 
     GemmProblem p;
     p.M = s.d_out;
@@ -354,7 +382,6 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
                            void* hip_stream) {
   DORA_CHECK(check_common(shape, DORA_OP_BACKWARD, ws, ws_bytes));
   const dora_shape& s = *shape;
-  if (s.flags & DORA_FLAG_EXACT_NORM_GRAD) return DORA_ERR_FLAGS;
   const bool noT = s.tokens == 0;
   DORA_CHECK(check_ptr(grad_y, noT));
   DORA_CHECK(check_ptr(x, noT));
@@ -373,14 +400,79 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   const int dt = s.dtype;
   const bool has_r = s.r > 0;
+  // Undetached norm (DoRA reading notes, Appendix A.1): only A and B see it.
+  const bool exact = (s.flags & DORA_FLAG_EXACT_NORM_GRAD) && has_r && (grad_A || grad_B);
 
   // gz = g * gy and the dm partial sums.
   void* gz = at(ws, L.gz);
   float* dmpart = reinterpret_cast<float*>(at(ws, L.dmpart));
   const bool need_gz = (grad_x && !noT) || (has_r && (grad_A || grad_B));
-  if (need_gz || grad_m)
+  float* dm = grad_m ? grad_m : (exact ? reinterpret_cast<float*>(at(ws, L.dm)) : nullptr);
+  if (need_gz || dm)
     HIP_TRY(compose_bwd(grad_y, y, m, norm, gz, dmpart, s.tokens, s.d_out, kTokPerDmBlock, dt, st));
-  if (grad_m) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, grad_m, s.d_out, dt, st));
+  if (dm) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, dt, st));
+
+  // A.1 terms: k' = -s m dm / n^2, Bk' = diag(k') B, Q = W0 A^T + s B G,
+  // H' = s Bk'^T B.  Then dB += diag(k') Q and dA += Bk'^T W0 + H' A.
+  float* kappa = nullptr;
+  void* bk = nullptr;
+  float* q = nullptr;
+  void* hmat = nullptr;
+  if (exact) {
+    kappa = reinterpret_cast<float*>(at(ws, L.kappa));
+    bk = at(ws, L.bk);
+    HIP_TRY(exact_prep(m, norm, dm, B, s.s, kappa, bk, s.d_out, s.r, dt, st));
+    float* gpart = reinterpret_cast<float*>(at(ws, L.egpart));
+    void* ghi = at(ws, L.eghi);
+    void* glo = at(ws, L.eglo);
+    GemmProblem g;
+    g.M = g.N = s.r;
+    g.nseg = 1;
+    g.seg[0] = {A, A, s.d_in, s.d_in, s.d_in};
+    g.c = gpart;
+    g.ldc = s.r;
+    g.out_f32 = true;
+    g.split = L.splits;
+    g.split_stride = s.r * s.r;
+    HIP_TRY(gemm(g, dt, st, "gram_AAt"));
+    HIP_TRY(gram_finalize(gpart, L.splits, s.r, s.s, dt, ghi, glo, st, "gram_finalize"));
+    q = reinterpret_cast<float*>(at(ws, L.q));
+    GemmProblem pq;
+    pq.M = s.d_out;
+    pq.N = s.r;
+    pq.seg[0] = {W0, A, s.d_in, s.d_in, s.d_in};
+    pq.seg[1] = {B, ghi, s.r, s.r, s.r};
+    pq.nseg = 2;
+    if (dt == kBF16) {
+      pq.seg[2] = {B, glo, s.r, s.r, s.r};
+      pq.nseg = 3;
+    }
+    pq.c = q;
+    pq.ldc = s.r;
+    pq.out_f32 = true;
+    pq.split = L.qsplits;
+    pq.split_stride = s.d_out * s.r;
+    HIP_TRY(gemm(pq, dt, st, "exact_q_proj"));
+    if (grad_A) {
+      float* hpart = reinterpret_cast<float*>(at(ws, L.hpart));
+      hmat = at(ws, L.hmat);
+      GemmProblem h;
+      h.M = h.N = s.r;
+      h.nseg = 1;
+      h.seg[0] = {bk, B, s.r, s.r, s.d_out};
+      h.a_kcontig = false;
+      h.b_kcontig = false;
+      h.alpha = s.s;
+      h.c = hpart;
+      h.ldc = s.r;
+      h.out_f32 = true;
+      h.split = L.hsplits;
+      h.split_stride = s.r * s.r;
+      HIP_TRY(gemm(h, dt, st, "exact_h_gram"));
+      HIP_TRY(gram_finalize(hpart, L.hsplits, s.r, 1.f, dt, hmat, at(ws, L.hlo), st,
+                            "exact_h_finalize"));
+    }
+  }
 
   // ts = s (gz B), needed by grad_x and grad_A.
   void* ts = at(ws, L.ts);
@@ -438,7 +530,17 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     b.c = grad_B;
     b.ldc = s.r;
     give_scratch(b, ws, L);
-    HIP_TRY(gemm(b, dt, st, "dB_gemm"));
+    if (exact) {   // float32 partial sums, combined with diag(k') Q in one rounding
+      float* d1 = reinterpret_cast<float*>(at(ws, L.d1));
+      b.c = d1;
+      b.out_f32 = true;
+      b.split = L.d1splits;
+      b.split_stride = s.d_out * s.r;
+      HIP_TRY(gemm(b, dt, st, "dB_gemm"));
+      HIP_TRY(db_combine(d1, L.d1splits, q, L.qsplits, kappa, grad_B, s.d_out, s.r, dt, st));
+    } else {
+      HIP_TRY(gemm(b, dt, st, "dB_gemm"));
+    }
   }
 
   if (grad_A && has_r) {
@@ -447,6 +549,11 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     a.N = s.d_in;
     a.nseg = 1;
     a.seg[0] = {ts, x, s.r, s.d_in, s.tokens};
+    if (exact) {   // [ts^T | Bk'^T | H'] [x ; W0 ; A]  (H' is symmetric)
+      a.seg[1] = {bk, W0, s.r, s.d_in, s.d_out};
+      a.seg[2] = {hmat, A, s.r, s.d_in, s.r};
+      a.nseg = 3;
+    }
     a.a_kcontig = false;
     a.b_kcontig = false;
     a.c = grad_A;

@@ -61,9 +61,19 @@ size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype, bool akc =
 hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* label);
 
 
-// G partial sums -> (s/2) * G; bf16: written as a hi + lo bf16 pair.
-hipError_t gram_finalize(const float* part, int splits, int64_t r, float s, int dtype,
-                         void* g_hi, void* g_lo, hipStream_t st);
+// scale * (sum of r x r partial sums); bf16: written as a hi + lo bf16 pair.
+hipError_t gram_finalize(const float* part, int splits, int64_t r, float scale, int dtype,
+                         void* g_hi, void* g_lo, hipStream_t st, const char* label);
+
+// Undetached norm gradient: k'_i = -s m_i dm_i / n_i^2 (float32) and Bk' = diag(k') B.
+hipError_t exact_prep(const void* m, const float* norm, const float* dm, const void* B, float s,
+                      float* kappa, void* Bk, int64_t d_out, int64_t r, int dtype,
+                      hipStream_t st);
+
+// dB = sum of d1 partials + k'_i * (sum of q partials), [d_out, r].
+hipError_t db_combine(const float* d1, int d1_splits, const float* q, int q_splits,
+                      const float* kappa, void* dB, int64_t d_out, int64_t r, int dtype,
+                      hipStream_t st);
 
 // n_i = sqrt(max(0, ||W0_i||^2 + B_i . P_i)), P = sum of p_splits partials
 // [p_splits][d_out][r] (float32).

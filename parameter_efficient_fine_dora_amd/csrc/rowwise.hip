@@ -266,16 +266,89 @@ __global__ __launch_bounds__(256) void dora_dm_finalize(const float* dm_part, in
     dm[i] = ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) / Vec<BF>::scalar(m, i);
 }
 
+// ---- undetached norm gradient (Appendix A.1 of the DoRA reading notes) -----------
+// Projecting dW'_i off V'_i adds -kappa_i V'_i to dV'_i with
+// kappa_i = m_i dm_i / n_i^2 (since dW'_i . V'_i = dm_i n_i).  Through
+// V' = W0 + s B A that gives dB_i += k'_i (W0 A^T + s B G)_i and
+// dA += Bk'^T W0 + s (Bk'^T B) A, with k' = -s kappa and Bk' = diag(k') B.
+// This kernel forms k' (float32) and Bk' (layer dtype).
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_exact_prep(const void* m, const float* norm,
+                                                       const float* dm, const void* B, float s,
+                                                       float* kappa, void* Bk, int64_t d_out,
+                                                       int64_t r) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = r > 0 ? idx / r : idx;
+  if (i >= d_out) return;
+  const float n = fmaxf(norm[i], kNormEps);
+  const float kp = -s * Vec<BF>::scalar(m, i) * dm[i] / (n * n);
+  if (r == 0 || idx % r == 0) kappa[i] = kp;
+  if (r > 0) {
+    const float b = Vec<BF>::scalar(B, idx);
+    if (BF)
+      reinterpret_cast<uint16_t*>(Bk)[idx] = f32_to_bf16(kp * b);
+    else
+      reinterpret_cast<float*>(Bk)[idx] = kp * b;
+  }
+}
+
+// dB = sum_z D1_z + k'_i * sum_z Q_z, each in a fixed order, rounded once.
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_db_combine(const float* d1, int d1_splits,
+                                                       const float* q, int q_splits,
+                                                       const float* kappa, void* dB, int64_t n,
+                                                       int64_t r) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  float a = 0.f, b = 0.f;
+  for (int z = 0; z < d1_splits; ++z) a += d1[z * n + idx];
+  for (int z = 0; z < q_splits; ++z) b += q[z * n + idx];
+  const float v = fmaf(kappa[idx / r], b, a);
+  if (BF)
+    reinterpret_cast<uint16_t*>(dB)[idx] = f32_to_bf16(v);
+  else
+    reinterpret_cast<float*>(dB)[idx] = v;
+}
+
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-hipError_t gram_finalize(const float* part, int splits, int64_t r, float s, int dtype, void* g_hi,
-                         void* g_lo, hipStream_t st) {
+hipError_t gram_finalize(const float* part, int splits, int64_t r, float scale, int dtype,
+                         void* g_hi, void* g_lo, hipStream_t st, const char* label) {
   if (r <= 0) return hipSuccess;
-  LaunchTimer t("gram_finalize", st);
+  LaunchTimer t(label, st);
   hipLaunchKernelGGL(dora_gram_finalize, dim3((unsigned)cdiv(r * r, 256)), dim3(256), 0, st, part,
-                     splits, r * r, 0.5f * s, dtype == kBF16 ? 1 : 0, g_hi, g_lo);
+                     splits, r * r, scale, dtype == kBF16 ? 1 : 0, g_hi, g_lo);
+  return hipGetLastError();
+}
+
+hipError_t exact_prep(const void* m, const float* norm, const float* dm, const void* B, float s,
+                      float* kappa, void* Bk, int64_t d_out, int64_t r, int dtype,
+                      hipStream_t st) {
+  LaunchTimer t("exact_prep", st);
+  const dim3 grid((unsigned)cdiv(d_out * (r > 0 ? r : 1), 256));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dora_exact_prep<true>, grid, dim3(256), 0, st, m, norm, dm, B, s, kappa, Bk,
+                       d_out, r);
+  else
+    hipLaunchKernelGGL(dora_exact_prep<false>, grid, dim3(256), 0, st, m, norm, dm, B, s, kappa,
+                       Bk, d_out, r);
+  return hipGetLastError();
+}
+
+hipError_t db_combine(const float* d1, int d1_splits, const float* q, int q_splits,
+                      const float* kappa, void* dB, int64_t d_out, int64_t r, int dtype,
+                      hipStream_t st) {
+  LaunchTimer t("dB_combine", st);
+  const int64_t n = d_out * r;
+  const dim3 grid((unsigned)cdiv(n, 256));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dora_db_combine<true>, grid, dim3(256), 0, st, d1, d1_splits, q, q_splits,
+                       kappa, dB, n, r);
+  else
+    hipLaunchKernelGGL(dora_db_combine<false>, grid, dim3(256), 0, st, d1, d1_splits, q, q_splits,
+                       kappa, dB, n, r);
   return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ def _norm(sh, W0=FAKE, A=FAKE, B=FAKE, out=FAKE, ws=FAKE, nb=1 << 40):
     ((64, 64, -8, 4), "DORA_ERR_SHAPE"), ((64, 64, 8, -1), "DORA_ERR_SHAPE"),
     ((60, 64, 8, 4), "DORA_ERR_SHAPE"), ((64, 66, 8, 4), "DORA_ERR_SHAPE"),
     ((64, 64, 12, 4), "DORA_ERR_SHAPE"), ((1 << 31, 8, 8, 4), "DORA_ERR_SHAPE"),
-    ((64, 64, 1 << 31, 8), "DORA_ERR_SHAPE"), ((64, 64, 8, 1 << 31), "DORA_ERR_SHAPE"),
+    ((1 << 22, 64, 8, 4), "DORA_ERR_SHAPE"), ((64, 1 << 22, 8, 4), "DORA_ERR_SHAPE"),
+    ((64, 64, 1 << 22, 8), "DORA_ERR_SHAPE"), ((64, 64, 8, 1 << 31), "DORA_ERR_SHAPE"),
 ])
 def test_bad_shapes_rejected(dims, code):
     sh = _lib.shape(*dims, _lib.BF16, 2.0)
@@ -86,12 +87,15 @@ def test_validation_codes():
     assert _norm(r0, W0=None, A=None, B=None) == _lib.ERR_CODE["DORA_ERR_NULL"]
 
 
-def test_backward_exact_flag_is_rejected_on_host():
-    sh = _lib.shape(64, 64, 8, 4, _lib.BF16, 2.0, _lib.FLAG_EXACT_NORM_GRAD)
-    nb = _lib.workspace_bytes(sh, _lib.OP_BACKWARD)
-    args = [FAKE] * 13
-    rc = _lib.lib().dora_backward(ctypes.byref(sh), *args, FAKE, nb, None)
-    assert rc == _lib.ERR_CODE["DORA_ERR_FLAGS"]
+def test_exact_flag_needs_its_own_workspace():
+    """The undetached gradient needs more workspace; the detached size is rejected for it."""
+    det = _lib.shape(64, 64, 8, 4, _lib.BF16, 2.0)
+    ex = _lib.shape(64, 64, 8, 4, _lib.BF16, 2.0, _lib.FLAG_EXACT_NORM_GRAD)
+    nb_det = _lib.workspace_bytes(det, _lib.OP_BACKWARD)
+    nb_ex = _lib.workspace_bytes(ex, _lib.OP_BACKWARD)
+    assert nb_ex > nb_det
+    rc = _lib.lib().dora_backward(ctypes.byref(ex), *([FAKE] * 13), FAKE, nb_det, None)
+    assert rc == _lib.ERR_CODE["DORA_ERR_WORKSPACE"]
 
 
 def test_workspace_never_scales_with_d_out_times_d_in():

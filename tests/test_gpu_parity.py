@@ -392,3 +392,65 @@ def test_dora_linear_module(ops):
     fresh = DoRALinear(dev["W0"], shape.r, shape.s)
     y0 = download(fresh(dev["x"]))
     check_out(y0, L["x"] @ L["W0"].T, "fresh module y = x W0^T")
+
+
+# ---- undetached norm gradient (DoRA reading notes, Appendix A.1) --------------------
+
+EXACT = [
+    ("ragged_bf16", LayerShape(264, 520, 24, 37, 2.0, "bf16"), 21, {}),
+    ("tiny_f32", synth.CONFIGS["tiny_f32"], 22, {}),
+    ("multitile_bf16", LayerShape(520, 1032, 136, 300, 2.0, "bf16"), 23, {}),
+    ("bigtile_ragged_bf16", LayerShape(776, 584, 72, 1031, 2.0, "bf16"), 24, {}),
+    ("largeB_bf16", LayerShape(264, 520, 24, 37, 2.0, "bf16"), 25, dict(b_std=0.1)),
+    ("sneg_f32", LayerShape(136, 200, 16, 9, -0.75, "f32"), 26, {}),
+    ("tokens0_bf16", LayerShape(136, 200, 16, 0, 2.0, "bf16"), 27, {}),
+]
+
+
+def aligned_grad_layer(shape, seed, kw):
+    """Layer whose upstream gradient leans on y, so the projection of eq. (A.1) matters."""
+    layer = synth.make_layer(shape, seed, grad=True, **kw)
+    if shape.tokens:
+        L = synth.layer_f64(layer, shape.dtype)
+        y, _ = oracle.dora_forward(L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
+        gy = L["gy"] + y / max(y.std(), 1e-30)
+        layer["gy"] = (synth.bf16_bits(gy.astype(np.float32)) if shape.dtype == "bf16"
+                       else gy.astype(np.float32))
+    return layer
+
+
+@pytest.mark.parametrize("flags", [1, 3], ids=["fused", "separate"])
+@pytest.mark.parametrize("name,shape,seed,kw", EXACT, ids=[c[0] for c in EXACT])
+def test_exact_norm_gradient(ops, name, shape, seed, kw, flags):
+    say(f"exact gradient {name} flags={flags}")
+    layer = aligned_grad_layer(shape, seed, kw)
+    got = run_layer(ops, shape, layer, flags=flags)
+    L = synth.layer_f64(layer, shape.dtype)
+    g = oracle.dora_backward(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s, exact=True)
+    for k in ("dx", "dA", "dB", "dm"):
+        if g[k].size:
+            check_out(got[k], g[k], "exact " + k)
+    if shape.tokens and shape.r:
+        # the detached result is measurably different here, so the flag is doing work
+        det = run_layer(ops, shape, layer, flags=flags & ~1)
+        err, scale, _ = out_stats(det["dB"], g["dB"])
+        assert err > 0.05 * scale, "detached and exact gradients should differ on this layer"
+
+
+def test_exact_norm_gradient_fullsize_sampled(ops):
+    name = "highrank_bwd_bf16"
+    shape = synth.CONFIGS[name]
+    say(f"full-size exact backward {name}")
+    layer = synth.make_layer(shape, synth.CONFIG_SEED[name], grad=True)
+    got = run_layer(ops, shape, layer, flags=1)
+    L = synth.layer_f64(layer, "bf16")
+    rng = np.random.Generator(np.random.PCG64(9))
+    tok = np.unique(_sample(rng, shape.tokens, 32))
+    rows = np.unique(_sample(rng, shape.d_out, 96))
+    cols = np.unique(_sample(rng, shape.d_in, 96))
+    ref = oracle.dora_backward_sampled(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s,
+                                       tok, rows, cols, exact=True)
+    check_out(got["dx"][tok], ref["dx"], "exact dx (sampled tokens)")
+    check_out(got["dB"][rows], ref["dB"], "exact dB (sampled rows)")
+    check_out(got["dA"][:, cols], ref["dA"], "exact dA (sampled columns)")
+    check_out(got["dm"][rows], ref["dm"], "exact dm (sampled rows)")
