@@ -43,6 +43,9 @@ struct KArgs {
   int kt_end[3];         // cumulative number of K tiles after each segment
   int kt_total;          // kt_end[nseg - 1], kept apart so no array is indexed at run time
   int kt_per_split;
+  int kq_end[3];         // the same in 32-deep steps (ring kernel)
+  int kq_total;
+  int kq_per_split;
   int tiles_m, tiles_n;
   void* c;
   int64_t ldc;
@@ -62,9 +65,17 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr uint32_t kOob = 0x80000000u;   // offset beyond every record: the load returns 0
 constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) buffer, gfx9-family data format
 
+// `base` and `bytes` must be wave-uniform: they are read from the first lane so
+// that the descriptor always lives in scalar registers (a descriptor the
+// compiler believes divergent would be wrapped in a per-lane loop).
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
   const int64_t b = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)b, kRsrcWord3);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int nb = __builtin_amdgcn_readfirstlane((int)b);
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, nb, kRsrcWord3);
 }
 __device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
@@ -282,6 +293,83 @@ __device__ __forceinline__ void wait_vmem_le() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Epilogue shared by the bf16 kernels: scale (and compose), then store.  bf16
+// outputs are staged through LDS so that every store is a whole 16-byte piece
+// of a row; float32 outputs (split-K partials) go straight out.
+template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
+__device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
+                                              uint8_t* smem, void* c, int64_t ldc,
+                                              int64_t split_stride, float alpha, const void* mag,
+                                              const float* nrm, int M, int N, int m0, int n0,
+                                              int wave, int wm, int wn, int lane) {
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int MB = TM / 32, NB = TN / 32;
+  constexpr int kStageLd = TN + 8;
+  // Epilogue.  acc[i][j][v]: m = m0 + wm*TM + i*32 + lane%32,
+  //                          n = n0 + wn*TN + j*32 + (v/4)*8 + (lane/32)*4 + v%4.
+  void* cbase = OUT_F32 ? (void*)(reinterpret_cast<float*>(c) + blockIdx.y * split_stride)
+                        : (void*)(reinterpret_cast<uint16_t*>(c) + blockIdx.y * split_stride);
+  if constexpr (!OUT_F32) {
+    // Stage the wave's tile in LDS (the K loop ended on a barrier, so every
+    // stage is free), then write whole 16-byte pieces of contiguous rows.
+    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * TM * kStageLd;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int nl = j * 32 + g * 8 + (lane >> 5) * 4;
+        const int n = n0 + wn * TN + nl;
+        f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
+        if (EPI == kEpiCompose && n < N) gm1 = gm1_4<true>(mag, nrm, n);
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int ml = i * 32 + (lane & 31);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float z = alpha * acc[i][j][g * 4 + e];
+            v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
+          }
+          *reinterpret_cast<u32x2*>(stg + ml * kStageLd + nl) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      }
+    }
+    constexpr int kChunksPerRow = TN / 8;
+#pragma unroll 4
+    for (int c = lane; c < TM * kChunksPerRow; c += 64) {
+      const int row = c / kChunksPerRow, ch = c - row * kChunksPerRow;
+      const int m = m0 + wm * TM + row, n = n0 + wn * TN + ch * 8;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stg + row * kStageLd + ch * 8);
+      if (m < M && n < N)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(cbase) + (int64_t)m * ldc + n) = val;
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = n0 + wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
+      if (n >= N) continue;
+      f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
+      if (EPI == kEpiCompose) gm1 = gm1_4<!OUT_F32>(mag, nrm, n);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int m = m0 + wm * TM + i * 32 + (lane & 31);
+        if (m >= M) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float z = alpha * acc[i][j][g * 4 + e];
+          v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
+        }
+        store4<OUT_F32>(cbase, ldc, m, n, v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32, int NST = 2>
 __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   constexpr int NT = WM * WN * 64;
@@ -422,73 +510,433 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   }
 #undef DORA_FETCH
 
-  // Epilogue.  acc[i][j][v]: m = m0 + wm*TM + i*32 + lane%32,
-  //                          n = n0 + wn*TN + j*32 + (v/4)*8 + (lane/32)*4 + v%4.
-  const int64_t ldc = p.ldc;
-  const float alpha = p.alpha;
-  const void* mag = p.mag;
-  const float* nrm = p.norm;
-  void* cbase = OUT_F32 ? (void*)(reinterpret_cast<float*>(p.c) + blockIdx.y * p.split_stride)
-                        : (void*)(reinterpret_cast<uint16_t*>(p.c) + blockIdx.y * p.split_stride);
-  if constexpr (!OUT_F32) {
-    // Stage the wave's tile in LDS (the K loop ended on a barrier, so every
-    // stage is free), then write whole 16-byte pieces of contiguous rows.
-    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * TM * kStageLd;
+  gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, smem, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
+                                                p.norm, M, N, m0, n0, wave, wm, wn, lane);
+}
+
+// ---- 32-deep ring pipeline (both operands K-contiguous) -----------------------
+// Four LDS slots of 32-deep K steps.  Step q's copies go out two iterations
+// before it is multiplied, in two halves placed between the MFMAs of the
+// previous step, so the copy engine works while the matrix cores do; one
+// barrier per step, without a memory fence, covers both the arrival of step
+// q+1 and the reuse of the slot step q-1 occupied.
+constexpr int kBKq = 32;            // K depth of one ring slot (bf16)
+constexpr int kRowQ = kBKq * 2;     // 64-byte LDS rows: four 16-byte chunks
+constexpr int kSlots = 4;
+
+// Chunk permutation for 64-byte rows: eight (and sixteen) consecutive rows
+// reading the same logical chunk land in distinct 16-byte bank slots of a
+// 128-byte (and 256-byte) window.
+__device__ __forceinline__ int swz4(int row) {
+  return (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1);
+}
+
+__device__ __forceinline__ bf16x8 lds_frag4(const uint8_t* lds, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(lds + row * kRowQ + ((chunk ^ swz4(row)) << 4));
+}
+
+// K-contiguous operand, R rows x 32 k per slot: one buffer_load ... lds fills
+// 16 rows x 64 bytes; lane l takes row l/4 and physical chunk l%4.
+template <int R, int NW>
+struct DmaQ {
+  static constexpr int kInstr = R / 16 / NW;   // per wave and slot
+  static_assert(R % (16 * NW) == 0, "rows must split evenly over the waves");
+  const uint16_t* base;
+  int64_t ld;
+  int64_t rows;
+  int K;
+  uint32_t off[kInstr];
+  uint32_t kcol[kInstr];
+  __device__ __forceinline__ void prepare(const uint16_t* p, int64_t ldv, int Kv, int row0,
+                                          int nrows, int wave, int lane) {
+    rows = nrows - row0;
+    if (rows > R) rows = R;
+    base = p + (int64_t)row0 * ldv;
+    ld = ldv;
+    K = Kv;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = j * 32 + g * 8 + (lane >> 5) * 4;
-        const int n = n0 + wn * TN + nl;
-        f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
-        if (EPI == kEpiCompose && n < N) gm1 = gm1_4<true>(mag, nrm, n);
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const int ml = i * 32 + (lane & 31);
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float z = alpha * acc[i][j][g * 4 + e];
-            v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
-          }
-          *reinterpret_cast<u32x2*>(stg + ml * kStageLd + nl) =
-              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        }
-      }
-    }
-    constexpr int kChunksPerRow = TN / 8;
-#pragma unroll 4
-    for (int c = lane; c < TM * kChunksPerRow; c += 64) {
-      const int row = c / kChunksPerRow, ch = c - row * kChunksPerRow;
-      const int m = m0 + wm * TM + row, n = n0 + wn * TN + ch * 8;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(stg + row * kStageLd + ch * 8);
-      if (m < M && n < N)
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(cbase) + (int64_t)m * ldc + n) = val;
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int n = n0 + wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
-      if (n >= N) continue;
-      f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
-      if (EPI == kEpiCompose) gm1 = gm1_4<!OUT_F32>(mag, nrm, n);
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int m = m0 + wm * TM + i * 32 + (lane & 31);
-        if (m >= M) continue;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float z = alpha * acc[i][j][g * 4 + e];
-          v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
-        }
-        store4<OUT_F32>(cbase, ldc, m, n, v[0], v[1], v[2], v[3]);
-      }
+    for (int i = 0; i < kInstr; ++i) {
+      const int row = (wave * kInstr + i) * 16 + (lane >> 2);
+      const int kc = (lane & 3) ^ swz4(row);
+      kcol[i] = (uint32_t)kc * 8u;
+      off[i] = (uint32_t)row * (uint32_t)(ldv * 2) + kcol[i] * 2u;
     }
   }
+  template <int I0, int I1>
+  __device__ __forceinline__ void issue(uint8_t* lds_tile, int k0, int wave) const {
+    if constexpr (I0 < I1) {
+      const Rsrc rs = make_rsrc(base + k0, rows * ld * 2 - (int64_t)k0 * 2);
+      const bool tail = k0 + kBKq > K;
+#pragma unroll
+      for (int i = I0; i < I1; ++i) {
+        const int rbase = (wave * kInstr + i) * 16;
+        const uint32_t o = (tail && (int)kcol[i] + k0 >= K) ? kOob : off[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(lds_tile + rbase * kRowQ), 16, (int)o,
+            0, 0, 0);
+      }
+    }
+  }
+};
+
+// s_barrier with no memory fence: the waits it needs are explicit.  The asm
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32, bool SPLITQ = true>
+__global__ __launch_bounds__(WM * WN * 64) void dora_gemm_ring(const KArgs p) {
+  constexpr int NW = WM * WN;
+  // SPLITQ: only the second half of the waves issue copies, so the first half
+  // never stalls on the copy queue and keeps the matrix cores fed meanwhile.
+  constexpr int NWC = SPLITQ ? NW / 2 : NW;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int MB = TM / 32, NB = TN / 32;
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  constexpr int ABYTES = BM * kRowQ, BBYTES = BN * kRowQ, STAGE = ABYTES + BBYTES;
+  constexpr int kStageLd = TN + 8;
+  constexpr int kOutBytes = OUT_F32 ? 0 : NW * TM * kStageLd * 2;
+  constexpr int kSmem = kSlots * STAGE > kOutBytes ? kSlots * STAGE : kOutBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
+  using DA = DmaQ<BM, NWC>;
+  using DB = DmaQ<BN, NWC>;
+  constexpr int kLoads = DA::kInstr + DB::kInstr;   // copies per wave and slot
+  constexpr int kHalfA = (DA::kInstr + 1) / 2, kHalfB = (DB::kInstr + 1) / 2;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WM, wn = wave / WM;
+  const bool loader = !SPLITQ || wave >= NW - NWC;
+  const int cwave = loader ? wave - (NW - NWC) : 0;   // index among the copying waves
+  const int M = p.M, N = p.N;
+  const int2 tc = tile_coords(p.tiles_m, p.tiles_n);
+  const int m0 = __builtin_amdgcn_readfirstlane(tc.x * BM);
+  const int n0 = __builtin_amdgcn_readfirstlane(tc.y * BN);
+  const int kq_end0 = p.kq_end[0], kq_end1 = p.kq_end[1];
+  const int kt_lo = blockIdx.y * p.kq_per_split;
+  const int kt_hi = min(kt_lo + p.kq_per_split, p.kq_total);
+  const uint16_t *a0 = p.a[0], *a1 = p.a[1], *a2 = p.a[2];
+  const uint16_t *b0 = p.b[0], *b1 = p.b[1], *b2 = p.b[2];
+  const int64_t lda0 = p.lda[0], lda1 = p.lda[1], lda2 = p.lda[2];
+  const int64_t ldb0 = p.ldb[0], ldb1 = p.ldb[1], ldb2 = p.ldb[2];
+  const int K0 = p.K[0], K1 = p.K[1], K2 = p.K[2];
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  DA ca;
+  DB cb;
+  int prep_seg = -1;
+  int k0n = 0;   // k offset (within its segment) of the step being copied
+  // Select the segment of step KT and prepare the copiers for it.
+#define DORA_RING_SEG(KT)                                                                  \
+  do {                                                                                     \
+    const int s_ = (KT) < kq_end0 ? 0 : ((KT) < kq_end1 ? 1 : 2);                          \
+    k0n = ((KT) - (s_ == 0 ? 0 : (s_ == 1 ? kq_end0 : kq_end1))) * kBKq;                   \
+    if (s_ != prep_seg) {                                                                  \
+      prep_seg = s_;                                                                       \
+      const int Ks_ = s_ == 0 ? K0 : (s_ == 1 ? K1 : K2);                                  \
+      ca.prepare(s_ == 0 ? a0 : (s_ == 1 ? a1 : a2), s_ == 0 ? lda0 : (s_ == 1 ? lda1 : lda2), \
+                 Ks_, m0, M, cwave, lane);                                                 \
+      cb.prepare(s_ == 0 ? b0 : (s_ == 1 ? b1 : b2), s_ == 0 ? ldb0 : (s_ == 1 ? ldb1 : ldb2), \
+                 Ks_, n0, N, cwave, lane);                                                 \
+    }                                                                                      \
+  } while (0)
+#define DORA_RING_COPY(SLOTP, H)                                                           \
+  do {                                                                                     \
+    if (loader) {                                                                          \
+      if ((H) == 0) {                                                                      \
+        ca.template issue<0, kHalfA>((SLOTP), k0n, cwave);                                 \
+        cb.template issue<0, kHalfB>((SLOTP) + ABYTES, k0n, cwave);                        \
+      } else {                                                                             \
+        ca.template issue<kHalfA, DA::kInstr>((SLOTP), k0n, cwave);                        \
+        cb.template issue<kHalfB, DB::kInstr>((SLOTP) + ABYTES, k0n, cwave);               \
+      }                                                                                    \
+    }                                                                                      \
+  } while (0)
+
+  bf16x8 af0[MB], bf0[NB], af1[MB], bf1[NB];
+#define DORA_RING_READ(AF, BFR, SLOTP, KK)                                                 \
+  do {                                                                                     \
+    const int ch_ = (KK) * 2 + (lane >> 5);                                                \
+    _Pragma("unroll") for (int i = 0; i < MB; ++i)                                         \
+        AF[i] = lds_frag4((SLOTP), wm * TM + i * 32 + (lane & 31), ch_);                  \
+    _Pragma("unroll") for (int j = 0; j < NB; ++j)                                         \
+        BFR[j] = lds_frag4((SLOTP) + ABYTES, wn * TN + j * 32 + (lane & 31), ch_);        \
+  } while (0)
+#define DORA_RING_MMA(AF, BFR)                                                             \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < MB; ++i)                                         \
+        _Pragma("unroll") for (int j = 0; j < NB; ++j) acc[i][j] =                         \
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(BFR[j], AF[i], acc[i][j], 0, 0, 0);   \
+  } while (0)
+
+  if (kt_lo < kt_hi) {
+    // Prologue: steps kt_lo .. kt_lo+2 into slots 0..2.
+#pragma unroll
+    for (int i = 0; i < kSlots - 1; ++i) {
+      if (kt_lo + i < kt_hi) {
+        DORA_RING_SEG(kt_lo + i);
+        DORA_RING_COPY(smem + i * STAGE, 0);
+        DORA_RING_COPY(smem + i * STAGE, 1);
+      }
+    }
+    if (kt_lo + 2 < kt_hi) wait_vmem_le<2 * kLoads>();
+    else if (kt_lo + 1 < kt_hi) wait_vmem_le<kLoads>();
+    else wait_vmem_le<0>();
+    barrier_nofence();
+    DORA_RING_READ(af0, bf0, smem, 0);
+    // One 32-deep step: MFMAs of its first half while its second half's fragments
+    // arrive; then (if there is a next step) wait for that step, barrier, send the
+    // first half of the copies of step kt+3 and read the next step's first
+    // fragments; then the second half's MFMAs and the rest of the copies.
+#define DORA_RING_STEP(HAS_NEXT, COPY, WAIT_LE)                                            \
+  do {                                                                                     \
+    const int rel_ = kt - kt_lo;                                                           \
+    const uint8_t* cur_ = smem + (rel_ & 3) * STAGE;                                       \
+    uint8_t* nxt_ = smem + ((rel_ + 1) & 3) * STAGE;                                       \
+    uint8_t* cpy_ = smem + ((rel_ + 3) & 3) * STAGE;                                       \
+    DORA_RING_READ(af1, bf1, cur_, 1);                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    DORA_RING_MMA(af0, bf0);                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    if (HAS_NEXT) {                                                                        \
+      wait_vmem_le<(WAIT_LE)>();                                                           \
+      barrier_nofence();                                                                   \
+      if (COPY) {                                                                          \
+        DORA_RING_SEG(kt + 3);                                                             \
+        DORA_RING_COPY(cpy_, 0);                                                           \
+      }                                                                                    \
+      DORA_RING_READ(af0, bf0, nxt_, 0);                                                   \
+    }                                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    DORA_RING_MMA(af1, bf1);                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    if (COPY) DORA_RING_COPY(cpy_, 1);                                                     \
+  } while (0)
+    int kt = kt_lo;
+    // steady state: a next step exists and step kt+3 is copied; step kt+2 may
+    // still be in flight when step kt+1 is waited for
+    for (; kt + 3 < kt_hi; ++kt) DORA_RING_STEP(true, true, kLoads);
+    // the last (up to) three steps
+    if (kt + 2 < kt_hi) {
+      DORA_RING_STEP(true, false, kLoads);
+      ++kt;
+    }
+    if (kt + 1 < kt_hi) {
+      DORA_RING_STEP(true, false, 0);
+      ++kt;
+    }
+    DORA_RING_STEP(false, false, 0);
+#undef DORA_RING_STEP
+    wait_vmem();
+    __syncthreads();   // every wave is done with the ring before the epilogue reuses it
+  }
+#undef DORA_RING_SEG
+#undef DORA_RING_COPY
+#undef DORA_RING_READ
+#undef DORA_RING_MMA
+
+  gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, smem, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
+                                                p.norm, M, N, m0, n0, wave, wm, wn, lane);
+}
+
+// ---- lean K-contiguous kernel ------------------------------------------------------
+// Both operands K-contiguous, copied straight to LDS, two 64-deep stages.  The
+// per-stage instruction stream is kept to the MFMAs, the fragment reads and the
+// copies: buffer descriptors and per-lane offsets are set once per K segment and
+// the K position travels in the scalar offset of each copy; only a segment's
+// last, partial step checks K per lane; LDS read addresses are per-lane bases
+// plus immediate offsets (the stage loop is unrolled by two).  With eight
+// waves per CU every scalar or vector instruction in the loop competes with
+// the MFMA issue, so this is what keeps the matrix cores busy.
+template <int R, int NW>
+struct LeanDma {
+  static constexpr int kInstr = R / 8 / NW;   // 16-byte copies per lane and stage
+  static_assert(R % (8 * NW) == 0, "rows must split evenly over the waves");
+  Rsrc rs;                 // tile base at k = 0, records = valid rows * ld * 2
+  uint32_t off[kInstr];    // row * ld * 2 + chunk * 16
+  __device__ __forceinline__ void prepare(const uint16_t* p, int64_t ld, int row0, int nrows,
+                                          int wave, int lane) {
+    int64_t rows = nrows - row0;
+    if (rows > R) rows = R;
+    rs = make_rsrc(p + (int64_t)row0 * ld, rows * ld * 2);
+#pragma unroll
+    for (int i = 0; i < kInstr; ++i) {
+      const int row = (wave * kInstr + i) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(row);
+      off[i] = (uint32_t)row * (uint32_t)(ld * 2) + (uint32_t)kc * 16u;
+    }
+  }
+  // Full step at byte column kbytes of the segment.
+  __device__ __forceinline__ void issue(uint8_t* lds_tile, int kbytes, int wave) const {
+#pragma unroll
+    for (int i = 0; i < kInstr; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds_tile + (wave * kInstr + i) * 8 * kRowBytes),
+          16, (int)off[i], kbytes, 0, 0);
+  }
+  // Partial step: chunks at or beyond K read as zeros.
+  __device__ __forceinline__ void issue_tail(uint8_t* lds_tile, int kbytes, int K, int wave,
+                                             int lane) const {
+#pragma unroll
+    for (int i = 0; i < kInstr; ++i) {
+      const int row = (wave * kInstr + i) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(row);
+      const bool in = kbytes / 2 + kc * 8 < K;
+      // kOob + kbytes stays below 2^32 and beyond every record count
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds_tile + (wave * kInstr + i) * 8 * kRowBytes),
+          16, (int)(in ? off[i] : kOob), kbytes, 0, 0);
+    }
+  }
+};
+
+template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
+__global__ __launch_bounds__(WM * WN * 64) void dora_gemm_kc(const KArgs p) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int MB = TM / 32, NB = TN / 32;
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  // LDS: [A stage 0 | A stage 1 | B stage 0 | B stage 1], so that every fragment
+  // read is a per-lane base plus an offset that fits the 16-bit immediate.
+  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes, STAGE = ABYTES + BBYTES;
+  constexpr int BBASE = 2 * ABYTES;
+  static_assert(ABYTES + (BM > 64 ? 64 * kRowBytes : 0) < 65536 && BBYTES < 65536,
+                "stage offsets must fit the LDS immediate");
+  constexpr int kStageLd = TN + 8;
+  constexpr int kOutBytes = OUT_F32 ? 0 : NW * TM * kStageLd * 2;
+  constexpr int kSmem = 2 * STAGE > kOutBytes ? 2 * STAGE : kOutBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
+  using DA = LeanDma<BM, NW>;
+  using DB = LeanDma<BN, NW>;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WM, wn = wave / WM;
+  const int M = p.M, N = p.N;
+  const int2 tc = tile_coords(p.tiles_m, p.tiles_n);
+  const int m0 = __builtin_amdgcn_readfirstlane(tc.x * BM);
+  const int n0 = __builtin_amdgcn_readfirstlane(tc.y * BN);
+  const int kt_lo = blockIdx.y * p.kt_per_split;
+  const int kt_hi = min(kt_lo + p.kt_per_split, p.kt_total);
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // Fragment read bases: the swizzle of row wm*TM + i*32 + lane%32 depends on i
+  // only through its parity, and the chunk of step kk only through an XOR.
+  uint32_t ra[2][4], rb[2][4];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int rowa = wm * TM + par * 32 + (lane & 31);
+      const int rowb = wn * TN + par * 32 + (lane & 31);
+      const int ch = kk * 2 + (lane >> 5);
+      ra[par][kk] = (uint32_t)(rowa * kRowBytes + ((ch ^ swz(rowa)) << 4));
+      rb[par][kk] = (uint32_t)(BBASE + rowb * kRowBytes + ((ch ^ swz(rowb)) << 4));
+    }
+
+  const int kt_end0 = p.kt_end[0], kt_end1 = p.kt_end[1], kt_end2 = p.kt_end[2];
+  const uint16_t *a0 = p.a[0], *a1 = p.a[1], *a2 = p.a[2];
+  const uint16_t *b0 = p.b[0], *b1 = p.b[1], *b2 = p.b[2];
+  const int64_t lda0 = p.lda[0], lda1 = p.lda[1], lda2 = p.lda[2];
+  const int64_t ldb0 = p.ldb[0], ldb1 = p.ldb[1], ldb2 = p.ldb[2];
+  const int K0 = p.K[0], K1 = p.K[1], K2 = p.K[2];
+
+  // Copies of K tile KT (relative tile KR of its segment) into stage buffer SB.
+#define DORA_KC_FETCH(KR, SB)                                                              \
+  do {                                                                                     \
+    const int kb_ = (KR) * (kBK * 2);                                                      \
+    uint8_t* sa_ = smem + (SB) * ABYTES;                                                   \
+    uint8_t* sb_ = smem + BBASE + (SB) * BBYTES;                                           \
+    if (partial && (KR) == last) {                                                         \
+      ca.issue_tail(sa_, kb_, Ks, wave, lane);                                             \
+      cb.issue_tail(sb_, kb_, Ks, wave, lane);                                             \
+    } else {                                                                               \
+      ca.issue(sa_, kb_, wave);                                                            \
+      cb.issue(sb_, kb_, wave);                                                            \
+    }                                                                                      \
+  } while (0)
+
+  bf16x8 af[2][MB], bfr[2][NB];
+#define DORA_KC_READ(SET, SB, KK)                                                          \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < MB; ++i) af[SET][i] =                            \
+        *reinterpret_cast<const bf16x8*>(smem + ra[i & 1][KK] + (i >> 1) * 64 * kRowBytes + \
+                                         (SB) * ABYTES);                                   \
+    _Pragma("unroll") for (int j = 0; j < NB; ++j) bfr[SET][j] =                           \
+        *reinterpret_cast<const bf16x8*>(smem + rb[j & 1][KK] + (j >> 1) * 64 * kRowBytes + \
+                                         (SB) * BBYTES);                                   \
+  } while (0)
+  // One stage: four 16-deep steps, fragments of step kk+1 read during step kk.
+#define DORA_KC_MMA(SB)                                                                    \
+  do {                                                                                     \
+    DORA_KC_READ(0, SB, 0);                                                                \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                     \
+      if (kk < 3) {                                                                        \
+        if (kk & 1) DORA_KC_READ(0, SB, kk + 1);                                           \
+        else DORA_KC_READ(1, SB, kk + 1);                                                  \
+      }                                                                                    \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i)                                       \
+          _Pragma("unroll") for (int j = 0; j < NB; ++j) acc[i][j] =                       \
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][j], af[kk & 1][i],      \
+                                                      acc[i][j], 0, 0, 0);                 \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+    }                                                                                      \
+  } while (0)
+
+  // Segments one after the other; the two-stage pipeline restarts at each
+  // (at most two restarts per launch), so within a segment the copy state is
+  // loop-invariant and stays in scalar registers.
+#pragma unroll 1
+  for (int seg = 0; seg < 3; ++seg) {
+    const int s_lo = seg == 0 ? 0 : (seg == 1 ? kt_end0 : kt_end1);
+    const int s_hi = seg == 0 ? kt_end0 : (seg == 1 ? kt_end1 : kt_end2);
+    const int lo = max(kt_lo, s_lo), hi = min(kt_hi, s_hi);
+    if (lo >= hi) continue;
+    const int Ks = seg == 0 ? K0 : (seg == 1 ? K1 : K2);
+    const bool partial = (Ks % kBK) != 0;
+    const int last = s_hi - 1 - s_lo;   // relative index of the segment's last tile
+    DA ca;
+    DB cb;
+    ca.prepare(seg == 0 ? a0 : (seg == 1 ? a1 : a2), seg == 0 ? lda0 : (seg == 1 ? lda1 : lda2),
+               m0, M, wave, lane);
+    cb.prepare(seg == 0 ? b0 : (seg == 1 ? b1 : b2), seg == 0 ? ldb0 : (seg == 1 ? ldb1 : ldb2),
+               n0, N, wave, lane);
+    const int r_lo = lo - s_lo, r_hi = hi - s_lo;
+    DORA_KC_FETCH(r_lo, 0);
+    wait_vmem();
+    barrier_nofence();
+    for (int kr = r_lo; kr < r_hi; kr += 2) {
+      if (kr + 1 < r_hi) DORA_KC_FETCH(kr + 1, 1);
+      DORA_KC_MMA(0);
+      wait_vmem();
+      barrier_nofence();
+      if (kr + 1 >= r_hi) break;
+      if (kr + 2 < r_hi) DORA_KC_FETCH(kr + 2, 0);
+      DORA_KC_MMA(1);
+      wait_vmem();
+      barrier_nofence();
+    }
+  }
+#undef DORA_KC_FETCH
+#undef DORA_KC_READ
+#undef DORA_KC_MMA
+
+  gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, smem, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
+                                                p.norm, M, N, m0, n0, wave, wm, wn, lane);
 }
 
 // float32 layers: 64x64 tiles, 16-deep K steps, 4x4 outputs per thread.
@@ -586,16 +1034,27 @@ __global__ __launch_bounds__(256) void dora_splitk_reduce(const float* part, int
 // ---- host-side dispatch -----------------------------------------------------
 
 // Tile configurations: BM x BN workgroup tile, WM x WN waves.
+// `ring`: the 32-deep four-slot pipeline (both operands K-contiguous only).
 struct Cfg {
   int bm, bn, wm, wn;
+  bool ring;
 };
 constexpr Cfg kCfgs[] = {
-    {256, 256, 2, 4},   // 0: 8 waves, 128x64 per wave
-    {256, 128, 2, 2},   // 1: 4 waves, 128x64 per wave
-    {128, 128, 2, 2},   // 2: 4 waves, 64x64 per wave
-    {128, 256, 2, 2},   // 3: 4 waves, 64x128 per wave
-    {64, 64, 2, 2},     // 4: 4 waves, 32x32 per wave
-    {256, 128, 4, 2},   // 5: 8 waves, 64x64 per wave
+    {256, 256, 2, 4, false},   // 0: 8 waves, 128x64 per wave
+    {256, 128, 2, 2, false},   // 1: 4 waves, 128x64 per wave
+    {128, 128, 2, 2, false},   // 2: 4 waves, 64x64 per wave
+    {128, 256, 2, 2, false},   // 3: 4 waves, 64x128 per wave
+    {64, 64, 2, 2, false},     // 4: 4 waves, 32x32 per wave
+    {256, 128, 4, 2, false},   // 5: 8 waves, 64x64 per wave
+    {256, 256, 2, 4, true},    // 6: ring, 8 waves, 128x64 per wave
+    {128, 128, 2, 2, true},    // 7: ring, 4 waves, 64x64 per wave
+    {256, 128, 4, 2, true},    // 8: ring, 8 waves, 64x64 per wave
+    {128, 256, 2, 2, true},    // 9: ring, 4 waves, 64x128 per wave
+    {256, 256, 2, 4, true},    // 10: ring, every wave copies
+    {128, 128, 2, 2, true},    // 11: ring, every wave copies
+    {256, 256, 2, 4, true},    // 12: lean K-contiguous, 8 waves, 128x64 per wave
+    {128, 128, 2, 2, true},    // 13: lean K-contiguous, 4 waves, 64x64 per wave
+    {256, 128, 4, 2, true},    // 14: lean K-contiguous, 8 waves, 64x64 per wave
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -630,6 +1089,35 @@ hipError_t launch_layout(bool akc, bool bkc, const KArgs& a, int epi, bool out_f
   return hipErrorInvalidValue;
 }
 
+template <int BM, int BN, int WM, int WN, bool SQ = true>
+hipError_t launch_ring(bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
+                       hipStream_t st) {
+  if (!(akc && bkc)) return hipErrorInvalidValue;
+  const dim3 block(WM * WN * 64);
+  if (out_f32)
+    hipLaunchKernelGGL((dora_gemm_ring<BM, BN, WM, WN, kEpiStore, true, SQ>), grid, block, 0, st, a);
+  else if (epi == kEpiCompose)
+    hipLaunchKernelGGL((dora_gemm_ring<BM, BN, WM, WN, kEpiCompose, false, SQ>), grid, block, 0, st,
+                       a);
+  else
+    hipLaunchKernelGGL((dora_gemm_ring<BM, BN, WM, WN, kEpiStore, false, SQ>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_kc(bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
+                     hipStream_t st) {
+  if (!(akc && bkc)) return hipErrorInvalidValue;
+  const dim3 block(WM * WN * 64);
+  if (out_f32)
+    hipLaunchKernelGGL((dora_gemm_kc<BM, BN, WM, WN, kEpiStore, true>), grid, block, 0, st, a);
+  else if (epi == kEpiCompose)
+    hipLaunchKernelGGL((dora_gemm_kc<BM, BN, WM, WN, kEpiCompose, false>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((dora_gemm_kc<BM, BN, WM, WN, kEpiStore, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
                       hipStream_t st) {
   switch (cfg) {
@@ -639,6 +1127,15 @@ hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool
     case 3: return launch_layout<128, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 4: return launch_layout<64, 64, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 5: return launch_layout<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 6: return launch_ring<256, 256, 2, 4>(akc, bkc, a, epi, out_f32, grid, st);
+    case 7: return launch_ring<128, 128, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 8: return launch_ring<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 9: return launch_ring<128, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 10: return launch_ring<256, 256, 2, 4, false>(akc, bkc, a, epi, out_f32, grid, st);
+    case 11: return launch_ring<128, 128, 2, 2, false>(akc, bkc, a, epi, out_f32, grid, st);
+    case 12: return launch_kc<256, 256, 2, 4>(akc, bkc, a, epi, out_f32, grid, st);
+    case 13: return launch_kc<128, 128, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 14: return launch_kc<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
 
     default: return hipErrorInvalidValue;
   }
@@ -660,7 +1157,7 @@ int fill_args(const GemmProblem& p, KArgs& a) {
   a = KArgs{};
   a.M = (int)p.M;
   a.N = (int)p.N;
-  int ns = 0, kt = 0;
+  int ns = 0, kt = 0, kq = 0;
   for (int s = 0; s < p.nseg; ++s) {
     if (p.seg[s].K <= 0) continue;
     a.a[ns] = reinterpret_cast<const uint16_t*>(p.seg[s].a);
@@ -669,17 +1166,24 @@ int fill_args(const GemmProblem& p, KArgs& a) {
     a.ldb[ns] = p.seg[s].ldb;
     a.K[ns] = (int)p.seg[s].K;
     kt += (int)cdiv64(p.seg[s].K, kBK);
+    kq += (int)cdiv64(p.seg[s].K, kBKq);
     a.kt_end[ns] = kt;
+    a.kq_end[ns] = kq;
     ++ns;
   }
   if (ns == 0) {  // empty K: C = 0 (one zero-length segment keeps the kernel uniform)
     a.K[0] = 0;
     a.kt_end[0] = 0;
+    a.kq_end[0] = 0;
     ns = 1;
   }
-  for (int s = ns; s < 3; ++s) a.kt_end[s] = kt;
+  for (int s = ns; s < 3; ++s) {
+    a.kt_end[s] = kt;
+    a.kq_end[s] = kq;
+  }
   a.nseg = ns;
   a.kt_total = kt;
+  a.kq_total = kq;
   a.c = p.c;
   a.ldc = p.ldc;
   a.split_stride = p.split_stride;
@@ -696,6 +1200,9 @@ hipError_t run(int cfg, int split, const GemmProblem& p, KArgs& a, int kt, hipSt
   a.tiles_n = (int)cdiv64(p.N, c.bn);
   a.kt_per_split = split > 1 ? (kt + split - 1) / split : (kt > 0 ? kt : 1);
   if (a.kt_per_split < 1) a.kt_per_split = 1;
+  const int kq = a.kq_total;
+  a.kq_per_split = split > 1 ? (kq + split - 1) / split : (kq > 0 ? kq : 1);
+  if (a.kq_per_split < 1) a.kq_per_split = 1;
   const dim3 grid(a.tiles_m * a.tiles_n, split);
   return launch_cfg(cfg, p.a_kcontig, p.b_kcontig, a, p.epi, out_f32, grid, st);
 }
@@ -706,14 +1213,15 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bk
   if (dtype == kF32 || M <= 0 || N <= 0) return {-1, 1};
   const int64_t ktiles = cdiv64(K, kBK);
   auto tiles = [&](int cfg) { return cdiv64(M, kCfgs[cfg].bm) * cdiv64(N, kCfgs[cfg].bn); };
-  // Large outputs: 256 x 256 tiles (8 waves), then 256 x 128 (8 waves).
-  if (tiles(0) >= 256) return {0, 1};
-  if (tiles(5) >= 200) return {5, 1};
+  const bool direct = akc && bkc;
+  // Large outputs: 256 x 256 tiles (8 waves), then 256 x 128 (8 waves); pairs of
+  // K-contiguous operands run the ring pipeline.
+  if (tiles(0) >= 256) return {direct ? 12 : 0, 1};
+  if (tiles(5) >= 200) return {direct ? 14 : 5, 1};
   // Skinny or small, split along K.  Measured on the d = 8192, r = 384 layer:
   // K-contiguous pairs do best on 128 x 128 tiles at ~384 workgroups, pairs
   // with a transposed operand on 256 x 256 tiles at ~256 workgroups.
-  const bool direct = akc && bkc;
-  const int cfg = direct ? 2 : 0;
+  const int cfg = direct ? 13 : 0;
   const int64_t target = direct ? 384 : 256;
   const int64_t t = tiles(cfg);
   int64_t split = (target + t / 2) / t;
