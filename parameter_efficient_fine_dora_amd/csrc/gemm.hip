@@ -8,20 +8,27 @@
 // up to three K segments are concatenated (e.g. [x | xs] . [W0 | B]^T).
 //
 // Tiling.  A workgroup owns a BM x BN output tile and walks K in 64-deep
-// steps through a double-buffered LDS stage.  LDS rows are 64 bf16 = 128 B,
-// split in eight 16-byte chunks whose order is XOR-swizzled by the row index
-// ((row & 7) ^ ((row >> 3) & 7)) so that the eight rows a 16-byte-per-lane
-// read or write touches land in distinct bank groups.  K-contiguous operands
-// are copied global -> registers -> LDS with 16-byte loads; M/N-contiguous
-// operands are loaded as 4(k) x 8(m) bf16 blocks and transposed in registers
-// before the store, so the MFMA fragment reads are the same for both.
-// Each wave computes a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  The
-// MFMA runs as D = opB-tile x opA-tile^T so that every lane ends up holding
-// four consecutive output columns (8-byte bf16 / 16-byte f32 stores).
+// steps through two LDS stages.  LDS rows are 64 bf16 = 128 B, split in eight
+// 16-byte chunks whose order is XOR-swizzled by the row index
+// ((row & 7) ^ ((row >> 3) & 7)) so that the eight (and sixteen) rows a
+// 16-byte-per-lane read or write touches land in distinct bank groups.
+// K-contiguous operands go global -> LDS directly (buffer_load ... lds);
+// M/N-contiguous operands are loaded as 4(k) x 8(m) bf16 blocks and
+// transposed in registers before the store, so the MFMA fragment reads are
+// the same for both.  Each wave computes a (BM/WM) x (BN/WN) sub-tile of
+// 32x32 MFMA blocks.  The MFMA runs as D = opB-tile x opA-tile^T so that every
+// lane ends up holding four consecutive output columns.
+//
+// Instruction budget.  With eight waves per CU every scalar or vector
+// instruction of the K loop competes with the MFMA issue, so the loop holds
+// little else: buffer descriptors and per-lane offsets are set once per K
+// segment, the K position travels in the scalar offset of each load, only a
+// segment's last partial step checks K per lane, and fragment reads are
+// per-lane bases plus immediate offsets (the stage loop is unrolled by two).
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 // remapped so that consecutive tiles (which share operand panels) run on
-// one XCD and share its L2, and tiles are walked in groups of 4 tile-rows.
+// one XCD and share its L2, and tiles are walked in groups of 8 tile-rows.
 #include <algorithm>
 
 #include "kernels.h"
@@ -43,9 +50,6 @@ struct KArgs {
   int kt_end[3];         // cumulative number of K tiles after each segment
   int kt_total;          // kt_end[nseg - 1], kept apart so no array is indexed at run time
   int kt_per_split;
-  int kq_end[3];         // the same in 32-deep steps (ring kernel)
-  int kq_total;
-  int kq_per_split;
   int tiles_m, tiles_n;
   void* c;
   int64_t ldc;
@@ -81,71 +85,75 @@ __device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// Operand views of one K segment (wave-uniform).
-struct OpView {
-  const uint16_t* p;
-  int64_t ld;
-  int K;
-};
+// ---- operand copiers ---------------------------------------------------------
+// Both keep their descriptor and per-lane offsets for a whole K segment; a
+// 64-deep step only supplies the scalar offset of its K position.
 
-// ---- global -> LDS copies ---------------------------------------------------
-
-// K-contiguous operand, R rows x 64 k, copied straight into LDS with
-// buffer_load ... lds: one wave instruction fills 8 rows x 128 B, lane l
-// takes row l/8 and physical chunk l%8, i.e. logical chunk (l%8) ^ swz(row).
-// Per-lane byte offsets are fixed for a K segment and computed once
-// (prepare); each 64-deep step only moves the scalar buffer base (issue).
+// K-contiguous operand, R rows x 64 k per stage, copied straight into LDS with
+// buffer_load ... lds: one wave instruction fills 8 rows x 128 B, lane l takes
+// row l/8 and physical chunk l%8, i.e. logical chunk (l%8) ^ swz(row).  Rows
+// past the operand are beyond the descriptor's records and read as zeros.
 template <int R, int NW>
-struct DmaKC {
-  static constexpr int kInstr = R / 8 / NW;   // per wave
+struct CopyKC {
+  static constexpr int kInstr = R / 8 / NW;   // 16-byte copies per lane and stage
   static_assert(R % (8 * NW) == 0, "rows must split evenly over the waves");
-  const uint16_t* base;   // operand rows of this tile, k = 0
-  int64_t ld;
-  int64_t rows;           // valid rows in the tile
-  int K;
-  uint32_t off[kInstr];   // row * ld * 2 + chunk * 16
-  uint32_t kcol[kInstr];  // chunk * 8 (k offset of the lane's 16 bytes)
-  __device__ __forceinline__ void prepare(const OpView& v, int row0, int nrows, int wave,
-                                          int lane) {
-    rows = nrows - row0;
+  // Instruction i of a wave fills rows (wave + i*NW)*8 .. +8.  With NW a
+  // multiple of 8 every instruction sees the same swizzle, so one per-lane
+  // offset serves them all and the row step goes into the scalar offset.
+  static constexpr bool kOne = NW % 8 == 0;
+  static constexpr int kOffs = kOne ? 1 : kInstr;
+  Rsrc rs;                 // tile base at k = 0, records = valid rows * ld * 2
+  uint32_t off[kOffs];     // row * ld * 2 + chunk * 16 (< 2^31: every dimension is < 2^22)
+  int step;                // bytes between instruction i and i+1 when kOne
+  __device__ __forceinline__ static int row_of(int i, int wave, int lane) {
+    return (wave + i * NW) * 8 + (lane >> 3);
+  }
+  __device__ __forceinline__ void prepare(const uint16_t* p, int64_t ld, int row0, int nrows, int,
+                                          int wave, int lane, int) {
+    int64_t rows = nrows - row0;
     if (rows > R) rows = R;
-    base = v.p + (int64_t)row0 * v.ld;
-    ld = v.ld;
-    K = v.K;
+    rs = make_rsrc(p + (int64_t)row0 * ld, rows * ld * 2);
+    step = NW * 8 * (int)(ld * 2);
 #pragma unroll
-    for (int i = 0; i < kInstr; ++i) {
-      const int row = (wave * kInstr + i) * 8 + (lane >> 3);
+    for (int i = 0; i < kOffs; ++i) {
+      const int row = row_of(i, wave, lane);
       const int kc = (lane & 7) ^ swz(row);
-      kcol[i] = (uint32_t)kc * 8u;
-      // 32-bit arithmetic: a tile spans < 2^31 bytes (the library limits every dimension)
-      off[i] = (uint32_t)row * (uint32_t)(v.ld * 2) + kcol[i] * 2u;
+      off[i] = (uint32_t)row * (uint32_t)(ld * 2) + (uint32_t)kc * 16u;
     }
   }
-  __device__ __forceinline__ void issue(uint8_t* lds_tile, int k0, int wave) const {
-    // rebased at column k0: rows past the tile's valid ones fall beyond the records
-    const Rsrc rs = make_rsrc(base + k0, rows * ld * 2 - (int64_t)k0 * 2);
-    const bool tail = k0 + kBK > K;   // uniform; only a segment's last step can be partial
+  // Step kt (relative to the segment) into the stage tile.  On a partial step
+  // the chunks at or beyond K read as zeros: kOob plus the scalar offset stays
+  // below 2^32 and beyond every record count.
+  template <bool TAIL>
+  __device__ __forceinline__ void issue(uint8_t* lds_tile, int kt, int K, int wave, int lane,
+                                        int) {
+    const int kbytes = kt * kRowBytes;
 #pragma unroll
     for (int i = 0; i < kInstr; ++i) {
-      const int rbase = (wave * kInstr + i) * 8;
-      const uint32_t o = (tail && (int)kcol[i] + k0 >= K) ? kOob : off[i];
+      uint32_t o = off[kOne ? 0 : i];
+      if (TAIL) {
+        const int row = row_of(i, wave, lane);
+        const int kc = (lane & 7) ^ swz(row);
+        if (kt * kBK + kc * 8 >= K) o = kOob;
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(lds_tile + rbase * kRowBytes), 16, (int)o,
-          0, 0, 0);
+          rs, (__attribute__((address_space(3))) void*)(lds_tile + (wave + i * NW) * 8 * kRowBytes),
+          16, (int)o, kbytes + (kOne ? i * step : 0), 0, 0);
     }
   }
+  __device__ __forceinline__ void commit(uint8_t*, int) {}
 };
 
-// M/N-contiguous operand: element (row, k) at p[k*ld + row].  Copied as
-// blocks of 4 consecutive k x 8 consecutive rows (four 16-byte loads),
-// transposed in registers into eight 8-byte row pieces.
+// M/N-contiguous operand: element (row, k) at p[k*ld + row].  Copied as blocks
+// of 4 consecutive k x 8 consecutive rows (four 16-byte loads), transposed in
+// registers into eight 8-byte row pieces.  Columns past the operand carry kOob
+// from the start; rows k past K are masked on a segment's last step only.
 template <int R, int NT>
-struct RegMC {
+struct CopyMC {
   static constexpr int kRowChunks = R / 8;
   static constexpr int kBlocks = kRowChunks * (kBK / 4);
   static constexpr int kPer = (kBlocks + NT - 1) / NT;
   static_assert(kRowChunks % 8 == 0, "block order assumes a multiple of 64 rows");
-  u32x4 v[kPer][4];
   // Block b -> (k-quad kq, row-chunk rc): eight consecutive blocks take eight
   // consecutive row chunks and the next eight the other half of the same
   // 16-byte k chunk, so sixteen lanes' 8-byte LDS writes fill sixteen distinct
@@ -156,34 +164,51 @@ struct RegMC {
     rc = (rest % kHi) * 8 + lo;
     kq = (rest / kHi) * 2 + kh;
   }
-  const uint16_t* base;    // column row0 of the operand, k = 0
+  Rsrc rs;
+  const uint16_t* base;    // column row0, k = kbase
   int64_t ld;
-  int K, row0, nrows;
-  __device__ __forceinline__ void prepare(const OpView& o, int r0, int nr, int) {
-    base = o.p + r0;
-    ld = o.ld;
-    K = o.K;
-    row0 = r0;
-    nrows = nr;
-  }
-  __device__ __forceinline__ void load(int k0, int tid) {
-    int64_t krows = K - k0;
-    if (krows > kBK) krows = kBK;
-    // rebased at row k0; rows k >= K fall past the end of the records
-    const Rsrc rs = make_rsrc(base + (int64_t)k0 * ld, krows * ld * 2 - (int64_t)row0 * 2);
-    const uint32_t ld2 = (uint32_t)(ld * 2);
+  int kt_base;             // step the descriptor starts at
+  int kt_span;             // steps one descriptor covers with a 31-bit scalar offset
+  uint32_t off[kPer];      // kq*4 * ld * 2 + rc * 16, or kOob; k row j adds j * ld * 2
+  u32x4 v[kPer][4];
+  __device__ __forceinline__ void prepare(const uint16_t* p, int64_t ldv, int row0, int nrows,
+                                          int K, int, int, int tid) {
+    base = p + row0;
+    ld = ldv;
+    kt_base = 0;
+    kt_span = (int)((int64_t)0x40000000 / (ldv * 2 * kBK));   // >= 2: ld < 2^22
+    rs = make_rsrc(base, (int64_t)K * ldv * 2);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int b = tid + i * NT;
       int kq, rc;
       block_of(b, kq, rc);
       const bool ok = (kBlocks % NT == 0 || b < kBlocks) && row0 + rc * 8 < nrows;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        v[i][j] = bload16(rs, ok ? (uint32_t)(kq * 4 + j) * ld2 + (uint32_t)rc * 16u : kOob);
+      off[i] = ok ? (uint32_t)(kq * 4) * (uint32_t)(ldv * 2) + (uint32_t)rc * 16u : kOob;
     }
   }
-  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+  template <bool TAIL>
+  __device__ __forceinline__ void issue(uint8_t*, int kt, int K, int, int, int tid) {
+    if (kt - kt_base >= kt_span) {   // keep the scalar offset below 2^30
+      kt_base = kt;
+      rs = make_rsrc(base + (int64_t)kt * kBK * ld, (int64_t)(K - kt * kBK) * ld * 2);
+    }
+    const int ld2 = (int)(ld * 2);
+    const int soff = (kt - kt_base) * kBK * ld2;   // < 2^30; plus 3 * ld2 < 2^31
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int kq = 0, rc = 0;
+      if (TAIL) block_of(tid + i * NT, kq, rc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t o = off[i];
+        if (TAIL && kt * kBK + kq * 4 + j >= K) o = kOob;
+        v[i][j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, soff + j * ld2, 0));
+      }
+    }
+  }
+  __device__ __forceinline__ void commit(uint8_t* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int b = tid + i * NT;
@@ -195,14 +220,10 @@ struct RegMC {
       for (int mm = 0; mm < 8; ++mm) {
         const int d = mm >> 1;
         const uint32_t a0 = v[i][0][d], a1 = v[i][1][d], a2 = v[i][2][d], a3 = v[i][3][d];
-        uint32_t lo, hi;
-        if (mm & 1) {
-          lo = (a0 >> 16) | (a1 & 0xffff0000u);
-          hi = (a2 >> 16) | (a3 & 0xffff0000u);
-        } else {
-          lo = (a0 & 0xffffu) | (a1 << 16);
-          hi = (a2 & 0xffffu) | (a3 << 16);
-        }
+        // bf16 element mm&1 of each of the four k rows, paired by byte permutes
+        const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(a1, a0, sel);
+        const uint32_t hi = __builtin_amdgcn_perm(a3, a2, sel);
         const int row = rc * 8 + mm;
         *reinterpret_cast<u32x2*>(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4) + half * 8) =
             u32x2{lo, hi};
@@ -211,36 +232,16 @@ struct RegMC {
   }
 };
 
-// Per-operand copy policy: K-contiguous operands go global -> LDS directly,
-// M/N-contiguous ones through registers (they are transposed on the way).
 template <int R, int NT, bool KC>
-struct Copier;
+struct CopyOp;
 template <int R, int NT>
-struct Copier<R, NT, true> {
-  DmaKC<R, NT / 64> d;
-  __device__ __forceinline__ void prepare(const OpView& o, int row0, int nrows, int tid, int wave,
-                                          int lane) {
-    d.prepare(o, row0, nrows, wave, lane);
-  }
-  __device__ __forceinline__ void issue(uint8_t* lds, int k0, int tid, int wave) {
-    d.issue(lds, k0, wave);
-  }
-  __device__ __forceinline__ void commit(uint8_t*, int) {}
+struct CopyOp<R, NT, true> : CopyKC<R, NT / 64> {
+  static constexpr bool kRegs = false;
 };
 template <int R, int NT>
-struct Copier<R, NT, false> {
-  RegMC<R, NT> r;
-  __device__ __forceinline__ void prepare(const OpView& o, int row0, int nrows, int tid, int,
-                                          int) {
-    r.prepare(o, row0, nrows, tid);
-  }
-  __device__ __forceinline__ void issue(uint8_t*, int k0, int tid, int) { r.load(k0, tid); }
-  __device__ __forceinline__ void commit(uint8_t* lds, int tid) { r.store(lds, tid); }
+struct CopyOp<R, NT, false> : CopyMC<R, NT> {
+  static constexpr bool kRegs = true;
 };
-
-__device__ __forceinline__ bf16x8 lds_frag(const uint8_t* lds, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4));
-}
 
 // Tile index -> (tile_m, tile_n), XCD-grouped, 8 tile-rows per group (an XCD's
 // 32 CUs then hold an ~8 x 4 block of tiles and share its operand panels in L2).
@@ -370,450 +371,30 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / W
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32, int NST = 2>
-__global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int MB = TM / 32, NB = TN / 32;
-  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(NST == 2 || (AKC && BKC), "deeper pipelines need both operands on the direct path");
-  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes, STAGE = ABYTES + BBYTES;
-  // bf16 outputs leave through LDS: each wave stages its TM x TN tile with rows
-  // padded by 8 elements (conflict-free 8-byte writes, 16-byte aligned reads)
-  constexpr int kStageLd = TN + 8;
-  constexpr int kOutBytes = OUT_F32 ? 0 : WM * WN * TM * kStageLd * 2;
-  constexpr int kSmem = NST * STAGE > kOutBytes ? NST * STAGE : kOutBytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % WM, wn = wave / WM;
-  const int M = p.M, N = p.N;
-  const int2 tc = tile_coords(p.tiles_m, p.tiles_n);
-  const int m0 = tc.x * BM, n0 = tc.y * BN;
-  const int kt_end0 = p.kt_end[0], kt_end1 = p.kt_end[1];
-  const int kt_lo = blockIdx.y * p.kt_per_split;
-  const int kt_hi = min(kt_lo + p.kt_per_split, p.kt_total);
-  const uint16_t *a0 = p.a[0], *a1 = p.a[1], *a2 = p.a[2];
-  const uint16_t *b0 = p.b[0], *b1 = p.b[1], *b2 = p.b[2];
-  const int64_t lda0 = p.lda[0], lda1 = p.lda[1], lda2 = p.lda[2];
-  const int64_t ldb0 = p.ldb[0], ldb1 = p.ldb[1], ldb2 = p.ldb[2];
-  const int K0 = p.K[0], K1 = p.K[1], K2 = p.K[2];
-
-  f32x16 acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  Copier<BM, NT, AKC> ca;
-  Copier<BN, NT, BKC> cb;
-  int prep_seg = -1;   // K segment the copiers are prepared for
-#define DORA_FETCH(KT, STAGE)                                                              \
-  do {                                                                                     \
-    const int s_ = (KT) < kt_end0 ? 0 : ((KT) < kt_end1 ? 1 : 2);                          \
-    const int k0_ = ((KT) - (s_ == 0 ? 0 : (s_ == 1 ? kt_end0 : kt_end1))) * kBK;          \
-    if (s_ != prep_seg) {                                                                  \
-      prep_seg = s_;                                                                       \
-      OpView va_, vb_;                                                                     \
-      va_.p = s_ == 0 ? a0 : (s_ == 1 ? a1 : a2);                                          \
-      va_.ld = s_ == 0 ? lda0 : (s_ == 1 ? lda1 : lda2);                                   \
-      va_.K = s_ == 0 ? K0 : (s_ == 1 ? K1 : K2);                                          \
-      vb_.p = s_ == 0 ? b0 : (s_ == 1 ? b1 : b2);                                          \
-      vb_.ld = s_ == 0 ? ldb0 : (s_ == 1 ? ldb1 : ldb2);                                   \
-      vb_.K = va_.K;                                                                       \
-      ca.prepare(va_, m0, M, tid, wave, lane);                                             \
-      cb.prepare(vb_, n0, N, tid, wave, lane);                                             \
-    }                                                                                      \
-    ca.issue((STAGE), k0_, tid, wave);                                                     \
-    cb.issue((STAGE) + ABYTES, k0_, tid, wave);                                            \
-  } while (0)
-
-  // One LDS stage: 4 steps of 16 k.  Fragments for step kk+1 are read while
-  // the MFMAs of step kk run (two register sets), so LDS latency hides behind
-  // the matrix cores instead of stalling them.
-  auto mma_stage = [&](const uint8_t* As) {
-    const uint8_t* Bs = As + ABYTES;
-    bf16x8 af[2][MB], bfg[2][NB];
-    auto read = [&](int set, int kk) {
-      const int ch = kk * 2 + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < MB; ++i) af[set][i] = lds_frag(As, wm * TM + i * 32 + (lane & 31), ch);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) bfg[set][j] = lds_frag(Bs, wn * TN + j * 32 + (lane & 31), ch);
-    };
-    read(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int cs = kk & 1;
-      if (kk + 1 < kBK / 16) read(cs ^ 1, kk + 1);
-      // keep the reads of step kk+1 ahead of the MFMAs of step kk
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[cs][j], af[cs][i], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  if constexpr (NST == 2) {
-    if (kt_lo < kt_hi) {
-      DORA_FETCH(kt_lo, smem);
-      ca.commit(smem, tid);
-      cb.commit(smem + ABYTES, tid);
-      wait_vmem();
-      __syncthreads();
-      for (int kt = kt_lo; kt < kt_hi; ++kt) {
-        const int cur = (kt - kt_lo) & 1;
-        const bool more = kt + 1 < kt_hi;
-        uint8_t* nx = smem + (cur ^ 1) * STAGE;
-        if (more) DORA_FETCH(kt + 1, nx);
-        mma_stage(smem + cur * STAGE);
-        if (more) {
-          ca.commit(nx, tid);
-          cb.commit(nx + ABYTES, tid);
-        }
-        wait_vmem();
-        __syncthreads();
-      }
-    }
-  } else {
-    // NST-stage ring, both operands copied straight to LDS: tile kt+NST-1 is
-    // in flight while tile kt is multiplied.
-    constexpr int kLoads = DmaKC<BM, NT / 64>::kInstr + DmaKC<BN, NT / 64>::kInstr;
-    static_assert(kLoads * (NST - 2) < 64, "outstanding loads exceed vmcnt");
-    if (kt_lo < kt_hi) {
-#pragma unroll
-      for (int i = 0; i < NST - 1; ++i)
-        if (kt_lo + i < kt_hi) DORA_FETCH(kt_lo + i, smem + i * STAGE);
-      wait_vmem();
-      __syncthreads();
-      int cur = 0;
-      for (int kt = kt_lo; kt < kt_hi; ++kt) {
-        const int ahead = kt + NST - 1;
-        int slot = cur + NST - 1;
-        if (slot >= NST) slot -= NST;
-        if (ahead < kt_hi) DORA_FETCH(ahead, smem + slot * STAGE);
-        mma_stage(smem + cur * STAGE);
-        if (ahead < kt_hi)
-          wait_vmem_le<kLoads * (NST - 2)>();   // tile kt+1 has landed
-        else
-          wait_vmem();
-        __syncthreads();
-        cur = cur + 1 == NST ? 0 : cur + 1;
-      }
-    }
-  }
-#undef DORA_FETCH
-
-  gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, smem, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
-                                                p.norm, M, N, m0, n0, wave, wm, wn, lane);
-}
-
-// ---- 32-deep ring pipeline (both operands K-contiguous) -----------------------
-// Four LDS slots of 32-deep K steps.  Step q's copies go out two iterations
-// before it is multiplied, in two halves placed between the MFMAs of the
-// previous step, so the copy engine works while the matrix cores do; one
-// barrier per step, without a memory fence, covers both the arrival of step
-// q+1 and the reuse of the slot step q-1 occupied.
-constexpr int kBKq = 32;            // K depth of one ring slot (bf16)
-constexpr int kRowQ = kBKq * 2;     // 64-byte LDS rows: four 16-byte chunks
-constexpr int kSlots = 4;
-
-// Chunk permutation for 64-byte rows: eight (and sixteen) consecutive rows
-// reading the same logical chunk land in distinct 16-byte bank slots of a
-// 128-byte (and 256-byte) window.
-__device__ __forceinline__ int swz4(int row) {
-  return (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1);
-}
-
-__device__ __forceinline__ bf16x8 lds_frag4(const uint8_t* lds, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(lds + row * kRowQ + ((chunk ^ swz4(row)) << 4));
-}
-
-// K-contiguous operand, R rows x 32 k per slot: one buffer_load ... lds fills
-// 16 rows x 64 bytes; lane l takes row l/4 and physical chunk l%4.
-template <int R, int NW>
-struct DmaQ {
-  static constexpr int kInstr = R / 16 / NW;   // per wave and slot
-  static_assert(R % (16 * NW) == 0, "rows must split evenly over the waves");
-  const uint16_t* base;
-  int64_t ld;
-  int64_t rows;
-  int K;
-  uint32_t off[kInstr];
-  uint32_t kcol[kInstr];
-  __device__ __forceinline__ void prepare(const uint16_t* p, int64_t ldv, int Kv, int row0,
-                                          int nrows, int wave, int lane) {
-    rows = nrows - row0;
-    if (rows > R) rows = R;
-    base = p + (int64_t)row0 * ldv;
-    ld = ldv;
-    K = Kv;
-#pragma unroll
-    for (int i = 0; i < kInstr; ++i) {
-      const int row = (wave * kInstr + i) * 16 + (lane >> 2);
-      const int kc = (lane & 3) ^ swz4(row);
-      kcol[i] = (uint32_t)kc * 8u;
-      off[i] = (uint32_t)row * (uint32_t)(ldv * 2) + kcol[i] * 2u;
-    }
-  }
-  template <int I0, int I1>
-  __device__ __forceinline__ void issue(uint8_t* lds_tile, int k0, int wave) const {
-    if constexpr (I0 < I1) {
-      const Rsrc rs = make_rsrc(base + k0, rows * ld * 2 - (int64_t)k0 * 2);
-      const bool tail = k0 + kBKq > K;
-#pragma unroll
-      for (int i = I0; i < I1; ++i) {
-        const int rbase = (wave * kInstr + i) * 16;
-        const uint32_t o = (tail && (int)kcol[i] + k0 >= K) ? kOob : off[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(lds_tile + rbase * kRowQ), 16, (int)o,
-            0, 0, 0);
-      }
-    }
-  }
-};
-
 // s_barrier with no memory fence: the waits it needs are explicit.  The asm
 // memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32, bool SPLITQ = true>
-__global__ __launch_bounds__(WM * WN * 64) void dora_gemm_ring(const KArgs p) {
-  constexpr int NW = WM * WN;
-  // SPLITQ: only the second half of the waves issue copies, so the first half
-  // never stalls on the copy queue and keeps the matrix cores fed meanwhile.
-  constexpr int NWC = SPLITQ ? NW / 2 : NW;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int MB = TM / 32, NB = TN / 32;
-  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  constexpr int ABYTES = BM * kRowQ, BBYTES = BN * kRowQ, STAGE = ABYTES + BBYTES;
-  constexpr int kStageLd = TN + 8;
-  constexpr int kOutBytes = OUT_F32 ? 0 : NW * TM * kStageLd * 2;
-  constexpr int kSmem = kSlots * STAGE > kOutBytes ? kSlots * STAGE : kOutBytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
-  using DA = DmaQ<BM, NWC>;
-  using DB = DmaQ<BN, NWC>;
-  constexpr int kLoads = DA::kInstr + DB::kInstr;   // copies per wave and slot
-  constexpr int kHalfA = (DA::kInstr + 1) / 2, kHalfB = (DB::kInstr + 1) / 2;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % WM, wn = wave / WM;
-  const bool loader = !SPLITQ || wave >= NW - NWC;
-  const int cwave = loader ? wave - (NW - NWC) : 0;   // index among the copying waves
-  const int M = p.M, N = p.N;
-  const int2 tc = tile_coords(p.tiles_m, p.tiles_n);
-  const int m0 = __builtin_amdgcn_readfirstlane(tc.x * BM);
-  const int n0 = __builtin_amdgcn_readfirstlane(tc.y * BN);
-  const int kq_end0 = p.kq_end[0], kq_end1 = p.kq_end[1];
-  const int kt_lo = blockIdx.y * p.kq_per_split;
-  const int kt_hi = min(kt_lo + p.kq_per_split, p.kq_total);
-  const uint16_t *a0 = p.a[0], *a1 = p.a[1], *a2 = p.a[2];
-  const uint16_t *b0 = p.b[0], *b1 = p.b[1], *b2 = p.b[2];
-  const int64_t lda0 = p.lda[0], lda1 = p.lda[1], lda2 = p.lda[2];
-  const int64_t ldb0 = p.ldb[0], ldb1 = p.ldb[1], ldb2 = p.ldb[2];
-  const int K0 = p.K[0], K1 = p.K[1], K2 = p.K[2];
-
-  f32x16 acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  DA ca;
-  DB cb;
-  int prep_seg = -1;
-  int k0n = 0;   // k offset (within its segment) of the step being copied
-  // Select the segment of step KT and prepare the copiers for it.
-#define DORA_RING_SEG(KT)                                                                  \
-  do {                                                                                     \
-    const int s_ = (KT) < kq_end0 ? 0 : ((KT) < kq_end1 ? 1 : 2);                          \
-    k0n = ((KT) - (s_ == 0 ? 0 : (s_ == 1 ? kq_end0 : kq_end1))) * kBKq;                   \
-    if (s_ != prep_seg) {                                                                  \
-      prep_seg = s_;                                                                       \
-      const int Ks_ = s_ == 0 ? K0 : (s_ == 1 ? K1 : K2);                                  \
-      ca.prepare(s_ == 0 ? a0 : (s_ == 1 ? a1 : a2), s_ == 0 ? lda0 : (s_ == 1 ? lda1 : lda2), \
-                 Ks_, m0, M, cwave, lane);                                                 \
-      cb.prepare(s_ == 0 ? b0 : (s_ == 1 ? b1 : b2), s_ == 0 ? ldb0 : (s_ == 1 ? ldb1 : ldb2), \
-                 Ks_, n0, N, cwave, lane);                                                 \
-    }                                                                                      \
-  } while (0)
-#define DORA_RING_COPY(SLOTP, H)                                                           \
-  do {                                                                                     \
-    if (loader) {                                                                          \
-      if ((H) == 0) {                                                                      \
-        ca.template issue<0, kHalfA>((SLOTP), k0n, cwave);                                 \
-        cb.template issue<0, kHalfB>((SLOTP) + ABYTES, k0n, cwave);                        \
-      } else {                                                                             \
-        ca.template issue<kHalfA, DA::kInstr>((SLOTP), k0n, cwave);                        \
-        cb.template issue<kHalfB, DB::kInstr>((SLOTP) + ABYTES, k0n, cwave);               \
-      }                                                                                    \
-    }                                                                                      \
-  } while (0)
-
-  bf16x8 af0[MB], bf0[NB], af1[MB], bf1[NB];
-#define DORA_RING_READ(AF, BFR, SLOTP, KK)                                                 \
-  do {                                                                                     \
-    const int ch_ = (KK) * 2 + (lane >> 5);                                                \
-    _Pragma("unroll") for (int i = 0; i < MB; ++i)                                         \
-        AF[i] = lds_frag4((SLOTP), wm * TM + i * 32 + (lane & 31), ch_);                  \
-    _Pragma("unroll") for (int j = 0; j < NB; ++j)                                         \
-        BFR[j] = lds_frag4((SLOTP) + ABYTES, wn * TN + j * 32 + (lane & 31), ch_);        \
-  } while (0)
-#define DORA_RING_MMA(AF, BFR)                                                             \
-  do {                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < MB; ++i)                                         \
-        _Pragma("unroll") for (int j = 0; j < NB; ++j) acc[i][j] =                         \
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(BFR[j], AF[i], acc[i][j], 0, 0, 0);   \
-  } while (0)
-
-  if (kt_lo < kt_hi) {
-    // Prologue: steps kt_lo .. kt_lo+2 into slots 0..2.
-#pragma unroll
-    for (int i = 0; i < kSlots - 1; ++i) {
-      if (kt_lo + i < kt_hi) {
-        DORA_RING_SEG(kt_lo + i);
-        DORA_RING_COPY(smem + i * STAGE, 0);
-        DORA_RING_COPY(smem + i * STAGE, 1);
-      }
-    }
-    if (kt_lo + 2 < kt_hi) wait_vmem_le<2 * kLoads>();
-    else if (kt_lo + 1 < kt_hi) wait_vmem_le<kLoads>();
-    else wait_vmem_le<0>();
-    barrier_nofence();
-    DORA_RING_READ(af0, bf0, smem, 0);
-    // One 32-deep step: MFMAs of its first half while its second half's fragments
-    // arrive; then (if there is a next step) wait for that step, barrier, send the
-    // first half of the copies of step kt+3 and read the next step's first
-    // fragments; then the second half's MFMAs and the rest of the copies.
-#define DORA_RING_STEP(HAS_NEXT, COPY, WAIT_LE)                                            \
-  do {                                                                                     \
-    const int rel_ = kt - kt_lo;                                                           \
-    const uint8_t* cur_ = smem + (rel_ & 3) * STAGE;                                       \
-    uint8_t* nxt_ = smem + ((rel_ + 1) & 3) * STAGE;                                       \
-    uint8_t* cpy_ = smem + ((rel_ + 3) & 3) * STAGE;                                       \
-    DORA_RING_READ(af1, bf1, cur_, 1);                                                     \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    DORA_RING_MMA(af0, bf0);                                                               \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    if (HAS_NEXT) {                                                                        \
-      wait_vmem_le<(WAIT_LE)>();                                                           \
-      barrier_nofence();                                                                   \
-      if (COPY) {                                                                          \
-        DORA_RING_SEG(kt + 3);                                                             \
-        DORA_RING_COPY(cpy_, 0);                                                           \
-      }                                                                                    \
-      DORA_RING_READ(af0, bf0, nxt_, 0);                                                   \
-    }                                                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    DORA_RING_MMA(af1, bf1);                                                               \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    if (COPY) DORA_RING_COPY(cpy_, 1);                                                     \
-  } while (0)
-    int kt = kt_lo;
-    // steady state: a next step exists and step kt+3 is copied; step kt+2 may
-    // still be in flight when step kt+1 is waited for
-    for (; kt + 3 < kt_hi; ++kt) DORA_RING_STEP(true, true, kLoads);
-    // the last (up to) three steps
-    if (kt + 2 < kt_hi) {
-      DORA_RING_STEP(true, false, kLoads);
-      ++kt;
-    }
-    if (kt + 1 < kt_hi) {
-      DORA_RING_STEP(true, false, 0);
-      ++kt;
-    }
-    DORA_RING_STEP(false, false, 0);
-#undef DORA_RING_STEP
-    wait_vmem();
-    __syncthreads();   // every wave is done with the ring before the epilogue reuses it
-  }
-#undef DORA_RING_SEG
-#undef DORA_RING_COPY
-#undef DORA_RING_READ
-#undef DORA_RING_MMA
-
-  gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, smem, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
-                                                p.norm, M, N, m0, n0, wave, wm, wn, lane);
-}
-
-// ---- lean K-contiguous kernel ------------------------------------------------------
-// Both operands K-contiguous, copied straight to LDS, two 64-deep stages.  The
-// per-stage instruction stream is kept to the MFMAs, the fragment reads and the
-// copies: buffer descriptors and per-lane offsets are set once per K segment and
-// the K position travels in the scalar offset of each copy; only a segment's
-// last, partial step checks K per lane; LDS read addresses are per-lane bases
-// plus immediate offsets (the stage loop is unrolled by two).  With eight
-// waves per CU every scalar or vector instruction in the loop competes with
-// the MFMA issue, so this is what keeps the matrix cores busy.
-template <int R, int NW>
-struct LeanDma {
-  static constexpr int kInstr = R / 8 / NW;   // 16-byte copies per lane and stage
-  static_assert(R % (8 * NW) == 0, "rows must split evenly over the waves");
-  Rsrc rs;                 // tile base at k = 0, records = valid rows * ld * 2
-  uint32_t off[kInstr];    // row * ld * 2 + chunk * 16
-  __device__ __forceinline__ void prepare(const uint16_t* p, int64_t ld, int row0, int nrows,
-                                          int wave, int lane) {
-    int64_t rows = nrows - row0;
-    if (rows > R) rows = R;
-    rs = make_rsrc(p + (int64_t)row0 * ld, rows * ld * 2);
-#pragma unroll
-    for (int i = 0; i < kInstr; ++i) {
-      const int row = (wave * kInstr + i) * 8 + (lane >> 3);
-      const int kc = (lane & 7) ^ swz(row);
-      off[i] = (uint32_t)row * (uint32_t)(ld * 2) + (uint32_t)kc * 16u;
-    }
-  }
-  // Full step at byte column kbytes of the segment.
-  __device__ __forceinline__ void issue(uint8_t* lds_tile, int kbytes, int wave) const {
-#pragma unroll
-    for (int i = 0; i < kInstr; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(lds_tile + (wave * kInstr + i) * 8 * kRowBytes),
-          16, (int)off[i], kbytes, 0, 0);
-  }
-  // Partial step: chunks at or beyond K read as zeros.
-  __device__ __forceinline__ void issue_tail(uint8_t* lds_tile, int kbytes, int K, int wave,
-                                             int lane) const {
-#pragma unroll
-    for (int i = 0; i < kInstr; ++i) {
-      const int row = (wave * kInstr + i) * 8 + (lane >> 3);
-      const int kc = (lane & 7) ^ swz(row);
-      const bool in = kbytes / 2 + kc * 8 < K;
-      // kOob + kbytes stays below 2^32 and beyond every record count
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(lds_tile + (wave * kInstr + i) * 8 * kRowBytes),
-          16, (int)(in ? off[i] : kOob), kbytes, 0, 0);
-    }
-  }
-};
-
-template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
-__global__ __launch_bounds__(WM * WN * 64) void dora_gemm_kc(const KArgs p) {
-  constexpr int NW = WM * WN;
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32>
+__global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
+  constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MB = TM / 32, NB = TN / 32;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   // LDS: [A stage 0 | A stage 1 | B stage 0 | B stage 1], so that every fragment
   // read is a per-lane base plus an offset that fits the 16-bit immediate.
-  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes, STAGE = ABYTES + BBYTES;
+  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
   constexpr int BBASE = 2 * ABYTES;
-  static_assert(ABYTES + (BM > 64 ? 64 * kRowBytes : 0) < 65536 && BBYTES < 65536,
+  static_assert(ABYTES + (MB > 2 ? 64 * kRowBytes : 0) < 65536 &&
+                    BBYTES + (NB > 2 ? 64 * kRowBytes : 0) < 65536,
                 "stage offsets must fit the LDS immediate");
   constexpr int kStageLd = TN + 8;
   constexpr int kOutBytes = OUT_F32 ? 0 : NW * TM * kStageLd * 2;
-  constexpr int kSmem = 2 * STAGE > kOutBytes ? 2 * STAGE : kOutBytes;
+  constexpr int kSmem = 2 * (ABYTES + BBYTES) > kOutBytes ? 2 * (ABYTES + BBYTES) : kOutBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
-  using DA = LeanDma<BM, NW>;
-  using DB = LeanDma<BN, NW>;
+  using CA = CopyOp<BM, NT, AKC>;
+  using CB = CopyOp<BN, NT, BKC>;
+  constexpr bool kRegs = CA::kRegs || CB::kRegs;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -824,6 +405,12 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_kc(const KArgs p) {
   const int n0 = __builtin_amdgcn_readfirstlane(tc.y * BN);
   const int kt_lo = blockIdx.y * p.kt_per_split;
   const int kt_hi = min(kt_lo + p.kt_per_split, p.kt_total);
+  const int kt_end0 = p.kt_end[0], kt_end1 = p.kt_end[1], kt_end2 = p.kt_end[2];
+  const uint16_t *a0 = p.a[0], *a1 = p.a[1], *a2 = p.a[2];
+  const uint16_t *b0 = p.b[0], *b1 = p.b[1], *b2 = p.b[2];
+  const int64_t lda0 = p.lda[0], lda1 = p.lda[1], lda2 = p.lda[2];
+  const int64_t ldb0 = p.ldb[0], ldb1 = p.ldb[1], ldb2 = p.ldb[2];
+  const int K0 = p.K[0], K1 = p.K[1], K2 = p.K[2];
 
   f32x16 acc[MB][NB];
 #pragma unroll
@@ -847,30 +434,31 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_kc(const KArgs p) {
       rb[par][kk] = (uint32_t)(BBASE + rowb * kRowBytes + ((ch ^ swz(rowb)) << 4));
     }
 
-  const int kt_end0 = p.kt_end[0], kt_end1 = p.kt_end[1], kt_end2 = p.kt_end[2];
-  const uint16_t *a0 = p.a[0], *a1 = p.a[1], *a2 = p.a[2];
-  const uint16_t *b0 = p.b[0], *b1 = p.b[1], *b2 = p.b[2];
-  const int64_t lda0 = p.lda[0], lda1 = p.lda[1], lda2 = p.lda[2];
-  const int64_t ldb0 = p.ldb[0], ldb1 = p.ldb[1], ldb2 = p.ldb[2];
-  const int K0 = p.K[0], K1 = p.K[1], K2 = p.K[2];
-
-  // Copies of K tile KT (relative tile KR of its segment) into stage buffer SB.
-#define DORA_KC_FETCH(KR, SB)                                                              \
+  // Copies of segment step KR into stage SB.
+#define DORA_FETCH(KR, SB)                                                                 \
   do {                                                                                     \
-    const int kb_ = (KR) * (kBK * 2);                                                      \
     uint8_t* sa_ = smem + (SB) * ABYTES;                                                   \
     uint8_t* sb_ = smem + BBASE + (SB) * BBYTES;                                           \
     if (partial && (KR) == last) {                                                         \
-      ca.issue_tail(sa_, kb_, Ks, wave, lane);                                             \
-      cb.issue_tail(sb_, kb_, Ks, wave, lane);                                             \
+      ca.template issue<true>(sa_, (KR), Ks, wave, lane, tid);                             \
+      cb.template issue<true>(sb_, (KR), Ks, wave, lane, tid);                             \
     } else {                                                                               \
-      ca.issue(sa_, kb_, wave);                                                            \
-      cb.issue(sb_, kb_, wave);                                                            \
+      ca.template issue<false>(sa_, (KR), Ks, wave, lane, tid);                            \
+      cb.template issue<false>(sb_, (KR), Ks, wave, lane, tid);                            \
+    }                                                                                      \
+  } while (0)
+  // Register-staged copies of stage SB land in LDS (after their loads).
+#define DORA_COMMIT(SB)                                                                    \
+  do {                                                                                     \
+    if (kRegs) {                                                                           \
+      wait_vmem();                                                                         \
+      ca.commit(smem + (SB) * ABYTES, tid);                                                \
+      cb.commit(smem + BBASE + (SB) * BBYTES, tid);                                        \
     }                                                                                      \
   } while (0)
 
   bf16x8 af[2][MB], bfr[2][NB];
-#define DORA_KC_READ(SET, SB, KK)                                                          \
+#define DORA_READ(SET, SB, KK)                                                             \
   do {                                                                                     \
     _Pragma("unroll") for (int i = 0; i < MB; ++i) af[SET][i] =                            \
         *reinterpret_cast<const bf16x8*>(smem + ra[i & 1][KK] + (i >> 1) * 64 * kRowBytes + \
@@ -880,13 +468,13 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_kc(const KArgs p) {
                                          (SB) * BBYTES);                                   \
   } while (0)
   // One stage: four 16-deep steps, fragments of step kk+1 read during step kk.
-#define DORA_KC_MMA(SB)                                                                    \
+#define DORA_MMA(SB)                                                                       \
   do {                                                                                     \
-    DORA_KC_READ(0, SB, 0);                                                                \
+    DORA_READ(0, SB, 0);                                                                   \
     _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                     \
       if (kk < 3) {                                                                        \
-        if (kk & 1) DORA_KC_READ(0, SB, kk + 1);                                           \
-        else DORA_KC_READ(1, SB, kk + 1);                                                  \
+        if (kk & 1) DORA_READ(0, SB, kk + 1);                                              \
+        else DORA_READ(1, SB, kk + 1);                                                     \
       }                                                                                    \
       __builtin_amdgcn_sched_barrier(0);                                                   \
       _Pragma("unroll") for (int i = 0; i < MB; ++i)                                       \
@@ -897,9 +485,9 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_kc(const KArgs p) {
     }                                                                                      \
   } while (0)
 
-  // Segments one after the other; the two-stage pipeline restarts at each
-  // (at most two restarts per launch), so within a segment the copy state is
-  // loop-invariant and stays in scalar registers.
+  // Segments one after the other; the two-stage pipeline restarts at each (at
+  // most two restarts per launch), so within a segment the copy state is
+  // loop-invariant.
 #pragma unroll 1
   for (int seg = 0; seg < 3; ++seg) {
     const int s_lo = seg == 0 ? 0 : (seg == 1 ? kt_end0 : kt_end1);
@@ -908,32 +496,36 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_kc(const KArgs p) {
     if (lo >= hi) continue;
     const int Ks = seg == 0 ? K0 : (seg == 1 ? K1 : K2);
     const bool partial = (Ks % kBK) != 0;
-    const int last = s_hi - 1 - s_lo;   // relative index of the segment's last tile
-    DA ca;
-    DB cb;
+    const int last = s_hi - 1 - s_lo;   // the segment's last step
+    CA ca;
+    CB cb;
     ca.prepare(seg == 0 ? a0 : (seg == 1 ? a1 : a2), seg == 0 ? lda0 : (seg == 1 ? lda1 : lda2),
-               m0, M, wave, lane);
+               m0, M, Ks, wave, lane, tid);
     cb.prepare(seg == 0 ? b0 : (seg == 1 ? b1 : b2), seg == 0 ? ldb0 : (seg == 1 ? ldb1 : ldb2),
-               n0, N, wave, lane);
+               n0, N, Ks, wave, lane, tid);
     const int r_lo = lo - s_lo, r_hi = hi - s_lo;
-    DORA_KC_FETCH(r_lo, 0);
+    DORA_FETCH(r_lo, 0);
+    DORA_COMMIT(0);
     wait_vmem();
     barrier_nofence();
     for (int kr = r_lo; kr < r_hi; kr += 2) {
-      if (kr + 1 < r_hi) DORA_KC_FETCH(kr + 1, 1);
-      DORA_KC_MMA(0);
+      if (kr + 1 < r_hi) DORA_FETCH(kr + 1, 1);
+      DORA_MMA(0);
+      if (kr + 1 < r_hi) DORA_COMMIT(1);
       wait_vmem();
       barrier_nofence();
       if (kr + 1 >= r_hi) break;
-      if (kr + 2 < r_hi) DORA_KC_FETCH(kr + 2, 0);
-      DORA_KC_MMA(1);
+      if (kr + 2 < r_hi) DORA_FETCH(kr + 2, 0);
+      DORA_MMA(1);
+      if (kr + 2 < r_hi) DORA_COMMIT(0);
       wait_vmem();
       barrier_nofence();
     }
   }
-#undef DORA_KC_FETCH
-#undef DORA_KC_READ
-#undef DORA_KC_MMA
+#undef DORA_FETCH
+#undef DORA_COMMIT
+#undef DORA_READ
+#undef DORA_MMA
 
   gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, smem, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
                                                 p.norm, M, N, m0, n0, wave, wm, wn, lane);
@@ -1034,49 +626,38 @@ __global__ __launch_bounds__(256) void dora_splitk_reduce(const float* part, int
 // ---- host-side dispatch -----------------------------------------------------
 
 // Tile configurations: BM x BN workgroup tile, WM x WN waves.
-// `ring`: the 32-deep four-slot pipeline (both operands K-contiguous only).
 struct Cfg {
   int bm, bn, wm, wn;
-  bool ring;
 };
 constexpr Cfg kCfgs[] = {
-    {256, 256, 2, 4, false},   // 0: 8 waves, 128x64 per wave
-    {256, 128, 2, 2, false},   // 1: 4 waves, 128x64 per wave
-    {128, 128, 2, 2, false},   // 2: 4 waves, 64x64 per wave
-    {128, 256, 2, 2, false},   // 3: 4 waves, 64x128 per wave
-    {64, 64, 2, 2, false},     // 4: 4 waves, 32x32 per wave
-    {256, 128, 4, 2, false},   // 5: 8 waves, 64x64 per wave
-    {256, 256, 2, 4, true},    // 6: ring, 8 waves, 128x64 per wave
-    {128, 128, 2, 2, true},    // 7: ring, 4 waves, 64x64 per wave
-    {256, 128, 4, 2, true},    // 8: ring, 8 waves, 64x64 per wave
-    {128, 256, 2, 2, true},    // 9: ring, 4 waves, 64x128 per wave
-    {256, 256, 2, 4, true},    // 10: ring, every wave copies
-    {128, 128, 2, 2, true},    // 11: ring, every wave copies
-    {256, 256, 2, 4, true},    // 12: lean K-contiguous, 8 waves, 128x64 per wave
-    {128, 128, 2, 2, true},    // 13: lean K-contiguous, 4 waves, 64x64 per wave
-    {256, 128, 4, 2, true},    // 14: lean K-contiguous, 8 waves, 64x64 per wave
+    {256, 256, 2, 4},   // 0: 8 waves, 128x64 per wave
+    {256, 128, 2, 2},   // 1: 4 waves, 128x64 per wave
+    {128, 128, 2, 2},   // 2: 4 waves, 64x64 per wave
+    {128, 256, 2, 2},   // 3: 4 waves, 64x128 per wave
+    {64, 64, 2, 2},     // 4: 4 waves, 32x32 per wave
+    {256, 128, 4, 2},   // 5: 8 waves, 64x64 per wave
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int NST = 2>
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC>
 hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStream_t st) {
   const dim3 block(WM * WN * 64);
   if (out_f32) {
-    hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, true, NST>), grid,
-                       block, 0, st, a);
+    hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, true>), grid, block, 0,
+                       st, a);
     return hipGetLastError();
   }
   if constexpr (AKC && BKC) {   // the compose epilogue belongs to the forward (K-contiguous) GEMM
     if (epi == kEpiCompose) {
-      hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiCompose, false, NST>), grid,
+      hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiCompose, false>), grid,
                          block, 0, st, a);
       return hipGetLastError();
     }
   } else {
     if (epi != kEpiStore) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, false, NST>), grid,
-                     block, 0, st, a);
+  hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, false>), grid, block, 0,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -1085,37 +666,10 @@ hipError_t launch_layout(bool akc, bool bkc, const KArgs& a, int epi, bool out_f
                          hipStream_t st) {
   if (akc && bkc) return launch_bf16<BM, BN, WM, WN, true, true>(a, epi, out_f32, grid, st);
   if (akc && !bkc) return launch_bf16<BM, BN, WM, WN, true, false>(a, epi, out_f32, grid, st);
-  if (!akc && !bkc) return launch_bf16<BM, BN, WM, WN, false, false>(a, epi, out_f32, grid, st);
+  // two register-staged operands do not fit beside a 256 x 256 tile's accumulators
+  if constexpr (BM * BN <= 256 * 128)
+    if (!akc && !bkc) return launch_bf16<BM, BN, WM, WN, false, false>(a, epi, out_f32, grid, st);
   return hipErrorInvalidValue;
-}
-
-template <int BM, int BN, int WM, int WN, bool SQ = true>
-hipError_t launch_ring(bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
-                       hipStream_t st) {
-  if (!(akc && bkc)) return hipErrorInvalidValue;
-  const dim3 block(WM * WN * 64);
-  if (out_f32)
-    hipLaunchKernelGGL((dora_gemm_ring<BM, BN, WM, WN, kEpiStore, true, SQ>), grid, block, 0, st, a);
-  else if (epi == kEpiCompose)
-    hipLaunchKernelGGL((dora_gemm_ring<BM, BN, WM, WN, kEpiCompose, false, SQ>), grid, block, 0, st,
-                       a);
-  else
-    hipLaunchKernelGGL((dora_gemm_ring<BM, BN, WM, WN, kEpiStore, false, SQ>), grid, block, 0, st, a);
-  return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_kc(bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
-                     hipStream_t st) {
-  if (!(akc && bkc)) return hipErrorInvalidValue;
-  const dim3 block(WM * WN * 64);
-  if (out_f32)
-    hipLaunchKernelGGL((dora_gemm_kc<BM, BN, WM, WN, kEpiStore, true>), grid, block, 0, st, a);
-  else if (epi == kEpiCompose)
-    hipLaunchKernelGGL((dora_gemm_kc<BM, BN, WM, WN, kEpiCompose, false>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((dora_gemm_kc<BM, BN, WM, WN, kEpiStore, false>), grid, block, 0, st, a);
-  return hipGetLastError();
 }
 
 hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
@@ -1127,16 +681,6 @@ hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool
     case 3: return launch_layout<128, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 4: return launch_layout<64, 64, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 5: return launch_layout<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 6: return launch_ring<256, 256, 2, 4>(akc, bkc, a, epi, out_f32, grid, st);
-    case 7: return launch_ring<128, 128, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 8: return launch_ring<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 9: return launch_ring<128, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 10: return launch_ring<256, 256, 2, 4, false>(akc, bkc, a, epi, out_f32, grid, st);
-    case 11: return launch_ring<128, 128, 2, 2, false>(akc, bkc, a, epi, out_f32, grid, st);
-    case 12: return launch_kc<256, 256, 2, 4>(akc, bkc, a, epi, out_f32, grid, st);
-    case 13: return launch_kc<128, 128, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 14: return launch_kc<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
-
     default: return hipErrorInvalidValue;
   }
 }
@@ -1157,7 +701,7 @@ int fill_args(const GemmProblem& p, KArgs& a) {
   a = KArgs{};
   a.M = (int)p.M;
   a.N = (int)p.N;
-  int ns = 0, kt = 0, kq = 0;
+  int ns = 0, kt = 0;
   for (int s = 0; s < p.nseg; ++s) {
     if (p.seg[s].K <= 0) continue;
     a.a[ns] = reinterpret_cast<const uint16_t*>(p.seg[s].a);
@@ -1166,24 +710,17 @@ int fill_args(const GemmProblem& p, KArgs& a) {
     a.ldb[ns] = p.seg[s].ldb;
     a.K[ns] = (int)p.seg[s].K;
     kt += (int)cdiv64(p.seg[s].K, kBK);
-    kq += (int)cdiv64(p.seg[s].K, kBKq);
     a.kt_end[ns] = kt;
-    a.kq_end[ns] = kq;
     ++ns;
   }
   if (ns == 0) {  // empty K: C = 0 (one zero-length segment keeps the kernel uniform)
     a.K[0] = 0;
     a.kt_end[0] = 0;
-    a.kq_end[0] = 0;
     ns = 1;
   }
-  for (int s = ns; s < 3; ++s) {
-    a.kt_end[s] = kt;
-    a.kq_end[s] = kq;
-  }
+  for (int s = ns; s < 3; ++s) a.kt_end[s] = kt;
   a.nseg = ns;
   a.kt_total = kt;
-  a.kq_total = kq;
   a.c = p.c;
   a.ldc = p.ldc;
   a.split_stride = p.split_stride;
@@ -1200,9 +737,6 @@ hipError_t run(int cfg, int split, const GemmProblem& p, KArgs& a, int kt, hipSt
   a.tiles_n = (int)cdiv64(p.N, c.bn);
   a.kt_per_split = split > 1 ? (kt + split - 1) / split : (kt > 0 ? kt : 1);
   if (a.kt_per_split < 1) a.kt_per_split = 1;
-  const int kq = a.kq_total;
-  a.kq_per_split = split > 1 ? (kq + split - 1) / split : (kq > 0 ? kq : 1);
-  if (a.kq_per_split < 1) a.kq_per_split = 1;
   const dim3 grid(a.tiles_m * a.tiles_n, split);
   return launch_cfg(cfg, p.a_kcontig, p.b_kcontig, a, p.epi, out_f32, grid, st);
 }
@@ -1213,16 +747,15 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bk
   if (dtype == kF32 || M <= 0 || N <= 0) return {-1, 1};
   const int64_t ktiles = cdiv64(K, kBK);
   auto tiles = [&](int cfg) { return cdiv64(M, kCfgs[cfg].bm) * cdiv64(N, kCfgs[cfg].bn); };
-  const bool direct = akc && bkc;
-  // Large outputs: 256 x 256 tiles (8 waves), then 256 x 128 (8 waves); pairs of
-  // K-contiguous operands run the ring pipeline.
-  if (tiles(0) >= 256) return {direct ? 12 : 0, 1};
-  if (tiles(5) >= 200) return {direct ? 14 : 5, 1};
-  // Skinny or small, split along K.  Measured on the d = 8192, r = 384 layer:
-  // K-contiguous pairs do best on 128 x 128 tiles at ~384 workgroups, pairs
-  // with a transposed operand on 256 x 256 tiles at ~256 workgroups.
-  const int cfg = direct ? 13 : 0;
-  const int64_t target = direct ? 384 : 256;
+  const bool both_mc = !akc && !bkc;
+  // Large outputs: 256 x 256 tiles (8 waves), then 256 x 128 (8 waves).  Two
+  // transposed operands take the 256 x 128 tile (register budget).
+  if (!both_mc && tiles(0) >= 256) return {0, 1};
+  if (tiles(5) >= 200) return {5, 1};
+  // Skinny or small, split along K: 128 x 128 tiles at ~384 workgroups did best
+  // for every operand layout of the d = 8192, r = 384 layer (xs, P, ts, dB, dA).
+  const int cfg = 2;
+  const int64_t target = 384;
   const int64_t t = tiles(cfg);
   int64_t split = (target + t / 2) / t;
   split = std::min<int64_t>(split, std::max<int64_t>(1, ktiles / 8));
