@@ -76,6 +76,7 @@ typedef struct {
 #define DORA_OP_NORM      0
 #define DORA_OP_FORWARD   1
 #define DORA_OP_BACKWARD  2
+#define DORA_OP_MERGE     3
 
 /* return codes */
 #define DORA_OK              0
@@ -89,7 +90,7 @@ typedef struct {
 
 /*
  * Bytes of device workspace `op` needs for `shape`: O(d_out*r + r*r + T*r)
- * for the norm and the GEMM-fused paths, plus one [T, d_out] buffer for the
+ * for the norm, merge and GEMM-fused paths, plus one [T, d_out] buffer for the
  * DORA_FLAG_SEPARATE_COMPOSE forward and for the backward; never d_out*d_in.
  * Returns 0 if the shape is invalid (the calls then fail with DORA_ERR_SHAPE).
  */
@@ -147,6 +148,24 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
                            const float* norm, const void* xs, const void* y,
                            void* grad_x, void* grad_A, void* grad_B, float* grad_m,
                            void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * Merged weight for deployment (DoRA reading notes, Algorithm 1 steps 16-17;
+ * Sec. 3.1 eq. (6)): the dense layer that replaces the adapted one,
+ *   W_out_i = g_i * (W0_i + s (B A)_i),  g_i = m_i / max(n_i, 1e-8),
+ * so that x W_out^T equals dora_forward's y.  One GEMM, B . A over K = r, whose
+ * epilogue adds W0 and scales each row; computed in float32, rounded once.
+ *   W0, A, B, m   inputs (layer dtype)
+ *   norm          float32 [d_out] as written by dora_norm / dora_forward, or NULL to
+ *                 compute it here (in the workspace)
+ *   W_out         output [d_out, d_in], layer dtype (the output is d_out x d_in by
+ *                 definition; it must not overlap any input)
+ *   ws            workspace of at least dora_workspace_bytes(shape, DORA_OP_MERGE)
+ * shape->tokens is not used.
+ */
+DORA_API int dora_merge(const dora_shape* shape, const void* W0, const void* A, const void* B,
+                        const void* m, const float* norm, void* W_out, void* ws, size_t ws_bytes,
+                        void* hip_stream);
 
 /* Static text for a DORA_* return code. */
 DORA_API const char* dora_strerror(int code);

@@ -86,6 +86,7 @@ struct Layout {
   size_t gpart = 0, ghi = 0, glo = 0, P = 0;     // norm
   size_t xs = 0, slora = 0;                      // forward
   size_t gz = 0, ts = 0, dmpart = 0;             // backward
+  size_t mnorm = 0;                              // merge: the row norms when not given
   // backward with the undetached norm gradient
   size_t dm = 0, kappa = 0, bk = 0, egpart = 0, eghi = 0, eglo = 0, q = 0, hpart = 0, hmat = 0,
          hlo = 0, d1 = 0;
@@ -111,13 +112,17 @@ Layout layout(const dora_shape& s, int op) {
   auto need = [&](int64_t M, int64_t N, int64_t K, bool akc = true, bool bkc = true) {
     scratch = std::max(scratch, gemm_scratch_bytes(M, N, K, dt, akc, bkc));
   };
-  if (op == DORA_OP_NORM || op == DORA_OP_FORWARD) {
+  if (op == DORA_OP_NORM || op == DORA_OP_FORWARD || op == DORA_OP_MERGE) {
     L.splits = gram_splits(s);
     L.psplits = p_splits(s);
     L.gpart = take((size_t)L.splits * r * r * 4);
     L.ghi = take(r * r * (s.dtype == kBF16 ? 2 : 4));
     L.glo = take(s.dtype == kBF16 ? r * r * 2 : 0);
     L.P = take((size_t)L.psplits * s.d_out * r * 4);
+  }
+  if (op == DORA_OP_MERGE) {
+    L.mnorm = take((size_t)s.d_out * 4);
+    need(s.d_out, s.d_in, s.r, true, false);
   }
   if (op == DORA_OP_FORWARD) {
     L.xs = take(T * r * e);
@@ -281,7 +286,7 @@ extern "C" {
 DORA_API size_t dora_workspace_bytes(const dora_shape* shape, int op) {
   if (!shape || (shape->dtype != DORA_F32 && shape->dtype != DORA_BF16) || !shape_ok(*shape))
     return 0;
-  if (op < DORA_OP_NORM || op > DORA_OP_BACKWARD) return 0;
+  if (op < DORA_OP_NORM || op > DORA_OP_MERGE) return 0;
   return layout(*shape, op).total;
 }
 
@@ -561,6 +566,47 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     give_scratch(a, ws, L);
     HIP_TRY(gemm(a, dt, st, "dA_gemm"));
   }
+  return DORA_OK;
+}
+
+DORA_API int dora_merge(const dora_shape* shape, const void* W0, const void* A, const void* B,
+                        const void* m, const float* norm, void* W_out, void* ws, size_t ws_bytes,
+                        void* hip_stream) {
+  DORA_CHECK(check_common(shape, DORA_OP_MERGE, ws, ws_bytes));
+  const dora_shape& s = *shape;
+  DORA_CHECK(check_ptr(W0, false));
+  DORA_CHECK(check_ptr(A, s.r == 0));
+  DORA_CHECK(check_ptr(B, s.r == 0));
+  DORA_CHECK(check_ptr(m, false));
+  DORA_CHECK(check_ptr(norm, true));
+  DORA_CHECK(check_ptr(W_out, false));
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  const Layout L = layout(s, DORA_OP_MERGE);
+  const int dt = s.dtype;
+  const float* n = norm;
+  if (!n) {
+    float* nn = reinterpret_cast<float*>(at(ws, L.mnorm));
+    DORA_CHECK(run_norm(s, W0, A, B, nn, ws, L, st));
+    n = nn;
+  }
+  // W_out = g (W0 + s B A): C[d_out, d_in] over K = r, A operand B (K-contiguous),
+  // B operand A read transposed (element (n, k) at A[k, n])
+  GemmProblem g;
+  g.M = s.d_out;
+  g.N = s.d_in;
+  g.nseg = 1;
+  g.seg[0] = {B, A, s.r, s.d_in, s.r};
+  g.a_kcontig = true;
+  g.b_kcontig = false;
+  g.c = W_out;
+  g.ldc = s.d_in;
+  g.alpha = s.s;
+  g.epi = kEpiMerge;
+  g.mag = m;
+  g.norm = n;
+  g.add = W0;
+  g.ld_add = s.d_in;
+  HIP_TRY(gemm(g, dt, st, "merge_gemm"));
   return DORA_OK;
 }
 

@@ -57,6 +57,8 @@ struct KArgs {
   float alpha;
   const void* mag;
   const float* norm;
+  const void* add;
+  int64_t ld_add;
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
@@ -285,6 +287,14 @@ __device__ __forceinline__ f32x4 gm1_4(const void* mag, const float* norm, int n
   return r;
 }
 
+// g for output row m (merge epilogue).
+template <bool BF>
+__device__ __forceinline__ float g_row(const void* mag, const float* norm, int m) {
+  const float mv = BF ? bf16_to_f32(reinterpret_cast<const uint16_t*>(mag)[m])
+                      : reinterpret_cast<const float*>(mag)[m];
+  return mv / fmaxf(norm[m], kNormEps);
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // s_waitcnt vmcnt(N) with the other counters left open (gfx9 encoding).
@@ -301,8 +311,9 @@ template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
 __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
                                               uint8_t* smem, void* c, int64_t ldc,
                                               int64_t split_stride, float alpha, const void* mag,
-                                              const float* nrm, int M, int N, int m0, int n0,
-                                              int wave, int wm, int wn, int lane) {
+                                              const float* nrm, const void* add, int64_t ld_add,
+                                              int M, int N, int m0, int n0, int wave, int wm,
+                                              int wn, int lane) {
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MB = TM / 32, NB = TN / 32;
   constexpr int kStageLd = TN + 8;
@@ -314,6 +325,12 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / W
     // Stage the wave's tile in LDS (the K loop ended on a barrier, so every
     // stage is free), then write whole 16-byte pieces of contiguous rows.
     uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * TM * kStageLd;
+    float grow[MB];   // merge: g of each of the lane's rows
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int m = m0 + wm * TM + i * 32 + (lane & 31);
+      grow[i] = (EPI == kEpiMerge && m < M) ? g_row<true>(mag, nrm, m) : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
 #pragma unroll
@@ -322,6 +339,15 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / W
         const int n = n0 + wn * TN + nl;
         f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
         if (EPI == kEpiCompose && n < N) gm1 = gm1_4<true>(mag, nrm, n);
+        u32x2 w[MB];   // merge: the addend's four values at (row, n..n+3)
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int m = m0 + wm * TM + i * 32 + (lane & 31);
+          w[i] = u32x2{0u, 0u};
+          if (EPI == kEpiMerge && m < M && n < N)
+            w[i] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(add) +
+                                                   (int64_t)m * ld_add + n);
+        }
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
           const int ml = i * 32 + (lane & 31);
@@ -329,7 +355,12 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / W
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float z = alpha * acc[i][j][g * 4 + e];
-            v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
+            if (EPI == kEpiMerge) {
+              const uint32_t wv = w[i][e >> 1];
+              v[e] = grow[i] * ((e & 1 ? bf_hi(wv) : bf_lo(wv)) + z);
+            } else {
+              v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
+            }
           }
           *reinterpret_cast<u32x2*>(stg + ml * kStageLd + nl) =
               u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -355,6 +386,7 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / W
       if (n >= N) continue;
       f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
       if (EPI == kEpiCompose) gm1 = gm1_4<!OUT_F32>(mag, nrm, n);
+      static_assert(EPI != kEpiMerge || !OUT_F32, "merge writes the layer dtype");
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int m = m0 + wm * TM + i * 32 + (lane & 31);
@@ -528,7 +560,8 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
 #undef DORA_MMA
 
   gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, smem, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
-                                                p.norm, M, N, m0, n0, wave, wm, wn, lane);
+                                                p.norm, p.add, p.ld_add, M, N, m0, n0, wave, wm,
+                                                wn, lane);
 }
 
 // float32 layers: 64x64 tiles, 16-deep K steps, 4x4 outputs per thread.
@@ -594,11 +627,17 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty * 4 + i;
     if (m >= p.M) continue;
+    f32x4 w = {0.f, 0.f, 0.f, 0.f};
+    float gr = 0.f;
+    if (EPI == kEpiMerge) {
+      w = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.add) + (int64_t)m * p.ld_add + n);
+      gr = g_row<false>(p.mag, p.norm, m);
+    }
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float z = p.alpha * acc[i][e];
-      v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
+      v[e] = (EPI == kEpiMerge) ? gr * (w[e] + z) : ((EPI == kEpiCompose) ? z + gm1[e] * z : z);
     }
     store4<true>(c, p.ldc, m, n, v[0], v[1], v[2], v[3]);
   }
@@ -653,6 +692,14 @@ hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStre
                          block, 0, st, a);
       return hipGetLastError();
     }
+    if (epi != kEpiStore) return hipErrorInvalidValue;
+  } else if constexpr (AKC && !BKC) {   // the merge epilogue belongs to B . A
+    if (epi == kEpiMerge) {
+      hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiMerge, false>), grid,
+                         block, 0, st, a);
+      return hipGetLastError();
+    }
+    if (epi != kEpiStore) return hipErrorInvalidValue;
   } else {
     if (epi != kEpiStore) return hipErrorInvalidValue;
   }
@@ -689,8 +736,12 @@ template <bool AKC, bool BKC>
 hipError_t launch_f32(const KArgs& a, int epi, dim3 grid, hipStream_t st) {
   if (epi == kEpiCompose)
     hipLaunchKernelGGL((dora_gemm_f32<AKC, BKC, kEpiCompose>), grid, dim3(256), 0, st, a);
-  else
+  else if (epi == kEpiMerge && AKC && !BKC)
+    hipLaunchKernelGGL((dora_gemm_f32<AKC, BKC, kEpiMerge>), grid, dim3(256), 0, st, a);
+  else if (epi == kEpiStore)
     hipLaunchKernelGGL((dora_gemm_f32<AKC, BKC, kEpiStore>), grid, dim3(256), 0, st, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -727,6 +778,8 @@ int fill_args(const GemmProblem& p, KArgs& a) {
   a.alpha = p.alpha;
   a.mag = p.mag;
   a.norm = p.norm;
+  a.add = p.add;
+  a.ld_add = p.ld_add;
   return kt;
 }
 

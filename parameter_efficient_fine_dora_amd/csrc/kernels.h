@@ -20,6 +20,7 @@ struct GemmSeg {
 enum Epilogue : int {
   kEpiStore = 0,     // C = alpha * acc
   kEpiCompose = 1,   // C = z + (g - 1) z with z = alpha * acc, g_n = m_n / max(norm_n, eps)
+  kEpiMerge = 2,     // C = g_m (add + alpha * acc) with g_m = m_m / max(norm_m, eps) per ROW
 };
 
 struct GemmProblem {
@@ -34,8 +35,10 @@ struct GemmProblem {
   int split = 1;               // split-K factor: C_z written at c + z*split_stride
   int64_t split_stride = 0;    // elements
   int epi = kEpiStore;
-  const void* mag = nullptr;   // kEpiCompose: m [N] (layer dtype)
-  const float* norm = nullptr; // kEpiCompose: n [N] float32
+  const void* mag = nullptr;   // kEpiCompose: m [N]; kEpiMerge: m [M] (layer dtype)
+  const float* norm = nullptr; // kEpiCompose: n [N]; kEpiMerge: n [M] (float32)
+  const void* add = nullptr;   // kEpiMerge: addend [M, N] (layer dtype), row stride ld_add
+  int64_t ld_add = 0;
   // Library-chosen split-K (layer-dtype store epilogue only): float32 partial
   // sums go to `scratch`, then a fixed-order reduction writes C.
   void* scratch = nullptr;

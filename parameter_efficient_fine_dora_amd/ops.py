@@ -160,6 +160,31 @@ def dora_backward(grad_y, x, W0, A, B, m, norm, xs, y, s, *, need=("x", "A", "B"
     return grad_x, grad_A, grad_B, grad_m
 
 
+def dora_merge(W0, A, B, m, s, *, norm=None, out=None, workspace=None):
+    """Merged weight g_i (W0_i + s (BA)_i) for deployment ([d_out, d_in], layer dtype).
+
+    ``norm`` (float32 [d_out], as from dora_norm / dora_forward) is computed when None.
+    """
+    dev = W0.device
+    dt = W0.dtype
+    d_out, d_in = W0.shape
+    r = A.shape[0]
+    _need(W0, "W0", dt)
+    _need(A, "A", dt, (r, d_in), dev)
+    _need(B, "B", dt, (d_out, r), dev)
+    _need(m, "m", dt, (d_out,), dev)
+    if norm is not None:
+        _need(norm, "norm", torch.float32, (d_out,), dev)
+    sh = _lib.shape(d_out, d_in, r, 0, _layer_dtype(W0), s)
+    if out is None:
+        out = torch.empty(d_out, d_in, dtype=dt, device=dev)
+    _need(out, "out", dt, (d_out, d_in), dev)
+    ws, nb = _ws(sh, _lib.OP_MERGE, dev, workspace)
+    _check(_lib.lib().dora_merge(ctypes.byref(sh), _ptr(W0), _ptr(A), _ptr(B), _ptr(m),
+                                 _ptr(norm), _ptr(out), _ptr(ws), nb, _stream(dev)), "dora_merge")
+    return out
+
+
 def timing_enable(on: bool = True):
     _lib.lib().dora_timing_enable(1 if on else 0)
 

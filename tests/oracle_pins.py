@@ -69,6 +69,9 @@ def pin_worked_rows(orc):
         if "y" in e:
             y, _ = orc.dora_forward(np.array(e["x"], float), W0, A, B, np.array(e["m"], float), s)
             _close(y, e["y"], 1e-15, e["name"] + " y")
+        if "merged" in e:
+            Wm = orc.merged_weight(W0, A, B, np.array(e["m"], float), s)
+            _close(Wm, e["merged"], 1e-15, e["name"] + " merged")
         if "gy" in e:
             gr = orc.dora_backward(np.array(e["gy"], float), np.array(e["x"], float), W0, A, B,
                                    np.array(e["m"], float), s)
@@ -245,8 +248,25 @@ def pin_sampled_forms(orc):
         _close(smp["dA"], full["dA"][:, cols], 1e-14, "dA cols")
 
 
+def pin_merged_weight(orc):
+    """The deploy-time merge (Alg. 1 step 16): every row of W'_merged has norm m_i and
+    direction V'_i; with B = 0 and m = ||W0_i|| it is W0 itself; x W'_merged^T is the
+    layer output."""
+    W0, A, B, m, x, _ = _layer(11)
+    s = 1.5
+    Wm = orc.merged_weight(W0, A, B, m, s)
+    _close(np.linalg.norm(Wm, axis=1), m, 1e-14, "merged rows have norm m")
+    V = W0 + s * (B @ A)
+    cosines = np.sum(Wm * V, axis=1) / (np.linalg.norm(Wm, axis=1) * np.linalg.norm(V, axis=1))
+    _close(cosines, np.ones_like(m), 1e-14, "merged rows point along V'")
+    Wb = orc.merged_weight(W0, A, np.zeros_like(B), np.linalg.norm(W0, axis=1), s)
+    _close(Wb, W0, 1e-14, "B=0, m=||W0_i|| merges to W0")
+    y, _ = orc.dora_forward(x, W0, A, B, m, s)
+    _close(x @ Wm.T, y, 1e-13, "x W'_merged^T is the layer output")
+
+
 ALL_PINS = [
     pin_worked_rows, pin_bruteforce, pin_factored_identity, pin_b_zero, pin_g_one_is_lora,
     pin_scale_invariance, pin_s_zero_weightnorm, pin_token_permutation, pin_fd_detached,
-    pin_fd_exact, pin_eq8_closed_form, pin_b_zero_backward, pin_sampled_forms,
+    pin_fd_exact, pin_eq8_closed_form, pin_b_zero_backward, pin_sampled_forms, pin_merged_weight,
 ]

@@ -21,7 +21,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     names = set(declared_symbols())
-    assert {"dora_norm", "dora_forward", "dora_backward", "dora_workspace_bytes",
+    assert {"dora_norm", "dora_forward", "dora_backward", "dora_merge", "dora_workspace_bytes",
             "dora_strerror", "dora_timing_enable", "dora_timing_collect"} <= names
 
 
@@ -85,6 +85,30 @@ def test_validation_codes():
     # a call that passes validation would enqueue kernels)
     r0 = _lib.shape(64, 64, 0, 4, _lib.BF16, 2.0)
     assert _norm(r0, W0=None, A=None, B=None) == _lib.ERR_CODE["DORA_ERR_NULL"]
+
+
+def test_merge_validation():
+    """dora_merge: every tensor but norm is required; its workspace comes from DORA_OP_MERGE."""
+    L = _lib.lib()
+    sh = _lib.shape(64, 64, 8, 0, _lib.BF16, 2.0)
+    need = _lib.workspace_bytes(sh, _lib.OP_MERGE)
+    assert need > 0
+
+    def merge(W0=FAKE, A=FAKE, B=FAKE, m=FAKE, norm=FAKE, out=FAKE, ws=FAKE, nb=need):
+        return L.dora_merge(ctypes.byref(sh), W0, A, B, m, norm, out, ws, nb, None)
+
+    for kw in ("W0", "A", "B", "m", "out", "ws"):
+        assert merge(**{kw: None}) == _lib.ERR_CODE["DORA_ERR_NULL"], kw
+    assert merge(out=FAKE + 4) == _lib.ERR_CODE["DORA_ERR_ALIGN"]
+    assert merge(norm=FAKE + 4) == _lib.ERR_CODE["DORA_ERR_ALIGN"]
+    assert merge(nb=need - 1) == _lib.ERR_CODE["DORA_ERR_WORKSPACE"]
+    bad = _lib.shape(64, 60, 8, 0, _lib.BF16, 2.0)
+    assert L.dora_merge(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, need,
+                        None) == _lib.ERR_CODE["DORA_ERR_SHAPE"]
+    # merge workspace: the norm's, plus the norms themselves; never d_out x d_in
+    big = _lib.shape(8192, 8192, 384, 0, _lib.BF16, 2.0)
+    assert (_lib.workspace_bytes(big, _lib.OP_MERGE) - _lib.workspace_bytes(big, _lib.OP_NORM)
+            <= 8192 * 4 + 1024)
 
 
 def test_exact_flag_needs_its_own_workspace():

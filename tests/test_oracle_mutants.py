@@ -33,6 +33,10 @@ MUTANTS = {
     "gram_single_s": ("gram = s * s * np.sum((B @ G) * B, axis=1)", "gram = s * np.sum((B @ G) * B, axis=1)"),
     "gram_transposed_operand": ("gram = s * s * np.sum((B @ G) * B, axis=1)",
                                 "gram = s * s * np.sum((B @ (A.T @ A)[:B.shape[1], :B.shape[1]]) * B, axis=1)"),
+    "merge_drops_g": ("    g = magnitude_scale(m, row_norms(V))\n    return g[:, None] * V",
+                      "    g = magnitude_scale(m, row_norms(V))\n    return V"),
+    "merge_scales_columns": ("    g = magnitude_scale(m, row_norms(V))\n    return g[:, None] * V",
+                             "    g = magnitude_scale(m, row_norms(V))\n    return V * np.resize(g, V.shape[1])[None, :]"),
     "sampled_rows_use_first_rows": ("V = _f64(W0[rows]) + float(s) * (_f64(B[rows]) @ _f64(A))\n    return row_norms(V)",
                                     "V = _f64(W0[:len(rows)]) + float(s) * (_f64(B[:len(rows)]) @ _f64(A))\n    return row_norms(V)"),
 }
