@@ -77,6 +77,7 @@ typedef struct {
 #define DORA_OP_FORWARD   1
 #define DORA_OP_BACKWARD  2
 #define DORA_OP_MERGE     3
+#define DORA_OP_VERA_GRADS 4
 
 /* return codes */
 #define DORA_OK              0
@@ -166,6 +167,28 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
 DORA_API int dora_merge(const dora_shape* shape, const void* W0, const void* A, const void* B,
                         const void* m, const float* norm, void* W_out, void* ws, size_t ws_bytes,
                         void* hip_stream);
+
+/*
+ * DVoRA (DoRA reading notes, Sec. 3.5): DoRA whose direction update is VeRA's
+ * diag(b) B_sh diag(d) A_sh, with A_sh [r, d_in] and B_sh [d_out, r] frozen
+ * random matrices shared by all layers and b [d_out], d [r] the trainable
+ * vectors of one layer.  It runs on the DoRA entry points with A = A_sh and
+ * B = B_eff = diag(b) B_sh diag(d):
+ *   dora_vera_scale    B_eff_ij = b_i B_sh_ij d_j   [d_out, r], layer dtype, rounded once
+ *   dora_forward / dora_backward with B = B_eff (grad_A may be NULL: A_sh is frozen;
+ *                      DORA_FLAG_EXACT_NORM_GRAD works unchanged)
+ *   dora_vera_grads    grad_b_i = sum_j grad_B_eff_ij B_sh_ij d_j   [d_out]
+ *                      grad_d_j = sum_i grad_B_eff_ij b_i B_sh_ij   [r]
+ *                      (layer dtype; float32 accumulation in a fixed order; either
+ *                      output may be NULL)
+ * Only d_out, r and dtype of `shape` are used (the rest must still be valid).
+ * dora_vera_grads needs dora_workspace_bytes(shape, DORA_OP_VERA_GRADS) bytes of ws.
+ */
+DORA_API int dora_vera_scale(const dora_shape* shape, const void* B_shared, const void* b,
+                             const void* d, void* B_eff, void* hip_stream);
+DORA_API int dora_vera_grads(const dora_shape* shape, const void* grad_B_eff,
+                             const void* B_shared, const void* b, const void* d, void* grad_b,
+                             void* grad_d, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Static text for a DORA_* return code. */
 DORA_API const char* dora_strerror(int code);

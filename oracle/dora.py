@@ -13,7 +13,7 @@ Sources (cited by page title and section):
         the factored base / cross / Gram terms.
   [DN]  DoRA reading notes (zhongzhuzhou.org): Sec. 3.1 eq. (6); Sec. 3.2
         Algorithm 1 (steps 7-18); Sec. 3.3 eq. (7), (8); Sec. 3.4 (detach);
-        Appendix A.1 eq. (A.1).
+        Sec. 3.5 (DVoRA: the direction update of VeRA); Appendix A.1 eq. (A.1).
 
 Conventions (readings where the pages disagree or are silent):
   * nn.Linear layout: W0 [d_out, d_in], A [r, d_in], B [d_out, r], x [T, d_in],
@@ -39,7 +39,7 @@ __all__ = [
     "NORM_EPS", "lora_update", "adapted_direction", "row_norms", "magnitude_scale",
     "dora_norm", "dora_forward", "dora_backward", "merged_weight", "norm_terms",
     "dora_norm_rows", "dora_forward_entries", "dora_backward_sampled",
-    "scaled_down_projection",
+    "scaled_down_projection", "vera_update", "dvora_forward", "dvora_backward",
 ]
 
 NORM_EPS = 1e-8
@@ -209,3 +209,56 @@ def dora_backward_sampled(gy, x, W0, A, B, m, s, tok, rows, cols, exact=False):
         dVc = g[:, None] * dWc
     out["dA"] = s * B.T @ dVc
     return out
+
+
+# ---- DVoRA ([DN] Sec. 3.5) -----------------------------------------------------
+# The direction update is VeRA's: a pair of frozen random matrices shared by all
+# layers, A_sh [r, d_in] and B_sh [d_out, r], and two trainable vectors per
+# layer, b [d_out] and d [r]:  Delta W = diag(b) B_sh diag(d) A_sh.  With the
+# scale s of the rest of this oracle: V' = W0 + s * Delta W.
+
+def vera_update(A_sh, B_sh, b, d):
+    """diag(b) @ B_sh @ diag(d) @ A_sh, formed densely ([DN] Sec. 3.5)."""
+    return np.diag(_f64(b)) @ _f64(B_sh) @ np.diag(_f64(d)) @ _f64(A_sh)
+
+
+def dvora_forward(x, W0, A_sh, B_sh, b, d, m, s):
+    """y = x @ W'^T with W' = m * V' / ||V'||_row and V' = W0 + s * vera_update.
+
+    Returns (y, n).  Forms V' directly from the VeRA product, not through an
+    effective B, so that the reduction to DoRA with B = diag(b) B_sh diag(d)
+    is something the pins check rather than assume.
+    """
+    V = _f64(W0) + float(s) * vera_update(A_sh, B_sh, b, d)
+    n = row_norms(V)
+    Wp = magnitude_scale(m, n)[:, None] * V
+    return _f64(x) @ Wp.T, n
+
+
+def dvora_backward(gy, x, W0, A_sh, B_sh, b, d, m, s, exact=False):
+    """Gradients of L = sum(gy * y) w.r.t. x, m and the VeRA vectors b, d.
+
+    A_sh and B_sh are frozen (shared, not trained).  dV' follows eq. (7) (or
+    A.1 with ``exact``), and Delta W = diag(b) B_sh diag(d) A_sh gives
+      db_i = s * sum_k dV'_ik (B_sh diag(d) A_sh)_ik
+      dd_j = s * sum_ik dV'_ik b_i B_sh_ij A_sh_jk.
+    Returns a dict with dx, dm, db, dd.
+    """
+    gy, x, W0 = _f64(gy), _f64(x), _f64(W0)
+    A_sh, B_sh, b, d, m = _f64(A_sh), _f64(B_sh), _f64(b), _f64(d), _f64(m)
+    s = float(s)
+    V = W0 + s * vera_update(A_sh, B_sh, b, d)
+    n = row_norms(V)
+    g = magnitude_scale(m, n)
+    dWp = gy.T @ x
+    along = np.sum(dWp * V, axis=1)
+    dm = along / np.maximum(n, NORM_EPS)
+    if exact:
+        dV = g[:, None] * (dWp - (along / np.maximum(n, NORM_EPS) ** 2)[:, None] * V)
+    else:
+        dV = g[:, None] * dWp
+    BdA = B_sh @ np.diag(d) @ A_sh
+    db = s * np.sum(dV * BdA, axis=1)
+    dd = s * np.einsum("ik,i,ij,jk->j", dV, b, B_sh, A_sh)
+    dx = gy @ (g[:, None] * V)
+    return {"dx": dx, "dm": dm, "db": db, "dd": dd}

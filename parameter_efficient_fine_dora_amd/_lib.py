@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(HERE, "libdora.so")
 F32, BF16 = 0, 1
 FLAG_EXACT_NORM_GRAD = 1 << 0
 FLAG_SEPARATE_COMPOSE = 1 << 1
-OP_NORM, OP_FORWARD, OP_BACKWARD, OP_MERGE = 0, 1, 2, 3
+OP_NORM, OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_VERA_GRADS = 0, 1, 2, 3, 4
 ERR = {0: "DORA_OK", -1: "DORA_ERR_NULL", -2: "DORA_ERR_SHAPE", -3: "DORA_ERR_DTYPE",
        -4: "DORA_ERR_ALIGN", -5: "DORA_ERR_WORKSPACE", -6: "DORA_ERR_HIP", -7: "DORA_ERR_FLAGS"}
 ERR_CODE = {v: k for k, v in ERR.items()}
@@ -41,6 +41,8 @@ _SIGS = {
     "dora_backward": (_i, [ctypes.POINTER(DoraShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dora_merge": (_i, [ctypes.POINTER(DoraShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dora_vera_scale": (_i, [ctypes.POINTER(DoraShape), _vp, _vp, _vp, _vp, _vp]),
+    "dora_vera_grads": (_i, [ctypes.POINTER(DoraShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dora_strerror": (ctypes.c_char_p, [_i]),
     "dora_timing_enable": (_i, [_i]),
     "dora_timing_collect": (_i, [ctypes.c_char_p, _sz]),

@@ -87,6 +87,7 @@ struct Layout {
   size_t xs = 0, slora = 0;                      // forward
   size_t gz = 0, ts = 0, dmpart = 0;             // backward
   size_t mnorm = 0;                              // merge: the row norms when not given
+  size_t vpart = 0;                              // DVoRA: row-block partials of grad_d
   // backward with the undetached norm gradient
   size_t dm = 0, kappa = 0, bk = 0, egpart = 0, eghi = 0, eglo = 0, q = 0, hpart = 0, hmat = 0,
          hlo = 0, d1 = 0;
@@ -120,6 +121,7 @@ Layout layout(const dora_shape& s, int op) {
     L.glo = take(s.dtype == kBF16 ? r * r * 2 : 0);
     L.P = take((size_t)L.psplits * s.d_out * r * 4);
   }
+  if (op == DORA_OP_VERA_GRADS) L.vpart = take((size_t)vera_dd_blocks(s.d_out) * r * 4);
   if (op == DORA_OP_MERGE) {
     L.mnorm = take((size_t)s.d_out * 4);
     need(s.d_out, s.d_in, s.r, true, false);
@@ -168,6 +170,9 @@ Layout layout(const dora_shape& s, int op) {
   L.total = off;
   return L;
 }
+
+// Validation-only op id of calls that take no workspace.
+constexpr int kOpNoWorkspace = -1;
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -286,7 +291,7 @@ extern "C" {
 DORA_API size_t dora_workspace_bytes(const dora_shape* shape, int op) {
   if (!shape || (shape->dtype != DORA_F32 && shape->dtype != DORA_BF16) || !shape_ok(*shape))
     return 0;
-  if (op < DORA_OP_NORM || op > DORA_OP_MERGE) return 0;
+  if (op < DORA_OP_NORM || op > DORA_OP_VERA_GRADS) return 0;
   return layout(*shape, op).total;
 }
 
@@ -607,6 +612,40 @@ DORA_API int dora_merge(const dora_shape* shape, const void* W0, const void* A, 
   g.add = W0;
   g.ld_add = s.d_in;
   HIP_TRY(gemm(g, dt, st, "merge_gemm"));
+  return DORA_OK;
+}
+
+DORA_API int dora_vera_scale(const dora_shape* shape, const void* B_shared, const void* b,
+                             const void* d, void* B_eff, void* hip_stream) {
+  DORA_CHECK(check_common(shape, kOpNoWorkspace, nullptr, 0));
+  const dora_shape& s = *shape;
+  const bool empty = s.r == 0;
+  DORA_CHECK(check_ptr(B_shared, empty));
+  DORA_CHECK(check_ptr(b, false));
+  DORA_CHECK(check_ptr(d, empty));
+  DORA_CHECK(check_ptr(B_eff, empty));
+  HIP_TRY(vera_scale(B_shared, b, d, B_eff, s.d_out, s.r, s.dtype,
+                     reinterpret_cast<hipStream_t>(hip_stream)));
+  return DORA_OK;
+}
+
+DORA_API int dora_vera_grads(const dora_shape* shape, const void* grad_B_eff,
+                             const void* B_shared, const void* b, const void* d, void* grad_b,
+                             void* grad_d, void* ws, size_t ws_bytes, void* hip_stream) {
+  DORA_CHECK(check_common(shape, DORA_OP_VERA_GRADS, ws, ws_bytes));
+  const dora_shape& s = *shape;
+  const bool empty = s.r == 0;
+  DORA_CHECK(check_ptr(grad_B_eff, empty));
+  DORA_CHECK(check_ptr(B_shared, empty));
+  DORA_CHECK(check_ptr(b, false));
+  DORA_CHECK(check_ptr(d, empty));
+  DORA_CHECK(check_ptr(grad_b, true));
+  DORA_CHECK(check_ptr(grad_d, true));
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  // with r == 0 every grad_b_i is an empty sum (written as 0) and grad_d is empty
+  const Layout L = layout(s, DORA_OP_VERA_GRADS);
+  HIP_TRY(vera_grads(grad_B_eff, B_shared, b, d, grad_b, grad_d,
+                     reinterpret_cast<float*>(at(ws, L.vpart)), s.d_out, s.r, s.dtype, st));
   return DORA_OK;
 }
 

@@ -74,6 +74,14 @@ hipError_t exact_prep(const void* m, const float* norm, const float* dm, const v
                       hipStream_t st);
 
 // dB = sum of d1 partials + k'_i * (sum of q partials), [d_out, r].
+// DVoRA: B_eff = diag(b) B_sh diag(d); db, dd from grad_B_eff (dd through
+// vera_dd_blocks(d_out) float32 row-block partials of r columns in `part`).
+hipError_t vera_scale(const void* Bsh, const void* b, const void* d, void* Be, int64_t d_out,
+                      int64_t r, int dtype, hipStream_t st);
+int64_t vera_dd_blocks(int64_t d_out);
+hipError_t vera_grads(const void* gBe, const void* Bsh, const void* b, const void* d, void* db,
+                      void* dd, float* part, int64_t d_out, int64_t r, int dtype, hipStream_t st);
+
 hipError_t db_combine(const float* d1, int d1_splits, const float* q, int q_splits,
                       const float* kappa, void* dB, int64_t d_out, int64_t r, int dtype,
                       hipStream_t st);

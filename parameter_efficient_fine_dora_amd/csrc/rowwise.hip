@@ -310,9 +310,130 @@ __global__ __launch_bounds__(256) void dora_db_combine(const float* d1, int d1_s
     reinterpret_cast<float*>(dB)[idx] = v;
 }
 
+// ---- DVoRA (DoRA reading notes, Sec. 3.5) --------------------------------------
+// The VeRA direction update diag(b) B_sh diag(d) A_sh enters the DoRA path as
+// the effective B = diag(b) B_sh diag(d); its gradient comes back as grad_B_eff
+// and splits into the two vectors:
+//   db_i = sum_j grad_B_eff_ij B_sh_ij d_j,   dd_j = sum_i grad_B_eff_ij b_i B_sh_ij.
+
+// B_eff = b_i * B_sh_ij * d_j, float32 product rounded once.
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_vera_scale(const void* Bsh, const void* b,
+                                                       const void* d, void* Be, int64_t n,
+                                                       int64_t r) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const float v = Vec<BF>::scalar(b, idx / r) * Vec<BF>::scalar(Bsh, idx) *
+                  Vec<BF>::scalar(d, idx % r);
+  if (BF)
+    reinterpret_cast<uint16_t*>(Be)[idx] = f32_to_bf16(v);
+  else
+    reinterpret_cast<float*>(Be)[idx] = v;
+}
+
+// db: one wave per row, lanes striding over the rank.
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_vera_db(const void* gBe, const void* Bsh,
+                                                    const void* d, void* db, int64_t d_out,
+                                                    int64_t r) {
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= d_out) return;
+  float acc = 0.f;
+  for (int64_t j = lane; j < r; j += 64)
+    acc += Vec<BF>::scalar(gBe, i * r + j) * Vec<BF>::scalar(Bsh, i * r + j) *
+           Vec<BF>::scalar(d, j);
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    if (BF)
+      reinterpret_cast<uint16_t*>(db)[i] = f32_to_bf16(acc);
+    else
+      reinterpret_cast<float*>(db)[i] = acc;
+  }
+}
+
+// dd, stage 1: each block sums kVeraRows consecutive rows of 256 columns, in order.
+constexpr int kVeraRows = 64;
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_vera_dd_part(const void* gBe, const void* Bsh,
+                                                         const void* b, float* part, int64_t d_out,
+                                                         int64_t r) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= r) return;
+  const int64_t i0 = (int64_t)blockIdx.y * kVeraRows;
+  const int64_t i1 = i0 + kVeraRows < d_out ? i0 + kVeraRows : d_out;
+  float acc = 0.f;
+  for (int64_t i = i0; i < i1; ++i)
+    acc += Vec<BF>::scalar(gBe, i * r + j) * Vec<BF>::scalar(Bsh, i * r + j) *
+           Vec<BF>::scalar(b, i);
+  part[blockIdx.y * r + j] = acc;
+}
+
+// dd, stage 2: the row-block partial sums of each column, in order.
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_vera_dd_final(const float* part, int64_t blocks,
+                                                          void* dd, int64_t r) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= r) return;
+  float acc = 0.f;
+  for (int64_t z = 0; z < blocks; ++z) acc += part[z * r + j];
+  if (BF)
+    reinterpret_cast<uint16_t*>(dd)[j] = f32_to_bf16(acc);
+  else
+    reinterpret_cast<float*>(dd)[j] = acc;
+}
+
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
+
+int64_t vera_dd_blocks(int64_t d_out) { return cdiv(d_out, kVeraRows); }
+
+hipError_t vera_scale(const void* Bsh, const void* b, const void* d, void* Be, int64_t d_out,
+                      int64_t r, int dtype, hipStream_t st) {
+  const int64_t n = d_out * r;
+  if (n <= 0) return hipSuccess;
+  LaunchTimer t("vera_scale", st);
+  const dim3 grid((unsigned)cdiv(n, 256));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dora_vera_scale<true>, grid, dim3(256), 0, st, Bsh, b, d, Be, n, r);
+  else
+    hipLaunchKernelGGL(dora_vera_scale<false>, grid, dim3(256), 0, st, Bsh, b, d, Be, n, r);
+  return hipGetLastError();
+}
+
+hipError_t vera_grads(const void* gBe, const void* Bsh, const void* b, const void* d, void* db,
+                      void* dd, float* part, int64_t d_out, int64_t r, int dtype,
+                      hipStream_t st) {
+  const bool bf = dtype == kBF16;
+  if (db && d_out > 0) {
+    LaunchTimer t("vera_db", st);
+    const dim3 grid((unsigned)cdiv(d_out, 4));
+    if (bf)
+      hipLaunchKernelGGL(dora_vera_db<true>, grid, dim3(256), 0, st, gBe, Bsh, d, db, d_out, r);
+    else
+      hipLaunchKernelGGL(dora_vera_db<false>, grid, dim3(256), 0, st, gBe, Bsh, d, db, d_out, r);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  if (dd && r > 0) {
+    LaunchTimer t("vera_dd", st);
+    const int64_t blocks = vera_dd_blocks(d_out);
+    if (blocks > 0) {
+      const dim3 g1((unsigned)cdiv(r, 256), (unsigned)blocks);
+      if (bf)
+        hipLaunchKernelGGL(dora_vera_dd_part<true>, g1, dim3(256), 0, st, gBe, Bsh, b, part, d_out, r);
+      else
+        hipLaunchKernelGGL(dora_vera_dd_part<false>, g1, dim3(256), 0, st, gBe, Bsh, b, part, d_out, r);
+    }
+    const dim3 g2((unsigned)cdiv(r, 256));
+    if (bf)
+      hipLaunchKernelGGL(dora_vera_dd_final<true>, g2, dim3(256), 0, st, part, blocks, dd, r);
+    else
+      hipLaunchKernelGGL(dora_vera_dd_final<false>, g2, dim3(256), 0, st, part, blocks, dd, r);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
 
 hipError_t gram_finalize(const float* part, int splits, int64_t r, float scale, int dtype,
                          void* g_hi, void* g_lo, hipStream_t st, const char* label) {

@@ -1,7 +1,8 @@
-"""DoRA linear layer on top of the C ABI (autograd glue only).
+"""DoRA and DVoRA linear layers on top of the C ABI (autograd glue only).
 
 Forward saves norm, xs = s (x A^T) and y for the backward; the norm is
-detached there (DoRA reading notes, Sec. 3.4).
+detached there (DoRA reading notes, Sec. 3.4).  DVoRA (Sec. 3.5) runs the same
+entry points with B = diag(b) B_shared diag(d).
 """
 from __future__ import annotations
 
@@ -59,4 +60,66 @@ class DoRALinear(torch.nn.Module):
         lead = x.shape[:-1]
         x2 = x.reshape(-1, x.shape[-1]).contiguous()
         y, _ = DoRAFunction.apply(x2, self.W0, self.A, self.B, self.m, self.s, self.flags)
+        return y.reshape(*lead, y.shape[-1])
+
+
+class DVoRAFunction(torch.autograd.Function):
+    """DoRA with VeRA's direction update: A_shared, B_shared frozen; b, d, m trained."""
+
+    @staticmethod
+    def forward(ctx, x, W0, A_sh, B_sh, b, d, m, s, flags):
+        Be = ops.dora_vera_scale(B_sh, b, d)
+        y, norm, xs = ops.dora_forward(x, W0, A_sh, Be, m, s, flags=flags)
+        ctx.s = s
+        ctx.flags = flags
+        ctx.save_for_backward(x, W0, A_sh, B_sh, b, d, Be, m, norm, xs, y)
+        return y
+
+    @staticmethod
+    def backward(ctx, gy):
+        x, W0, A_sh, B_sh, b, d, Be, m, norm, xs, y = ctx.saved_tensors
+        want_vec = ctx.needs_input_grad[4] or ctx.needs_input_grad[5]
+        need = tuple(n for n, ok in (("x", ctx.needs_input_grad[0]), ("B", want_vec),
+                                      ("m", ctx.needs_input_grad[6])) if ok)
+        gx, _, gBe, gm = ops.dora_backward(gy.contiguous(), x, W0, A_sh, Be, m, norm, xs, y, ctx.s,
+                                           need=need, flags=ctx.flags)
+        gb = gd = None
+        if want_vec:
+            gb, gd = ops.dora_vera_grads(gBe, B_sh, b, d)
+        if gm is not None:
+            gm = gm.to(m.dtype)
+        return gx, None, None, None, gb, gd, gm, None, None
+
+
+class DVoRALinear(torch.nn.Module):
+    """DVoRA layer: y = (m / ||V'||_row) x V'^T, V' = W0 + s diag(b) B_sh diag(d) A_sh.
+
+    A_shared [r, d_in] and B_shared [d_out, r] are frozen (shared by every layer
+    of a model); the trainable vectors start at b = 0 (the update starts at zero,
+    as DoRA's B = 0 does) and d = d_init, with m = ||W0_i||.
+    """
+
+    def __init__(self, weight, A_shared, B_shared, s: float = 1.0, d_init: float = 0.1,
+                 flags: int = 0):
+        super().__init__()
+        d_out, d_in = weight.shape
+        r = A_shared.shape[0]
+        dev, dt = weight.device, weight.dtype
+        self.register_buffer("W0", weight.detach().contiguous())
+        self.register_buffer("A_shared", A_shared.detach().contiguous())
+        self.register_buffer("B_shared", B_shared.detach().contiguous())
+        self.b = torch.nn.Parameter(torch.zeros(d_out, device=dev, dtype=dt))
+        self.d = torch.nn.Parameter(torch.full((r,), float(d_init), device=dev, dtype=dt))
+        self.m = torch.nn.Parameter(torch.empty(d_out, device=dev, dtype=dt))
+        with torch.no_grad():
+            Be = ops.dora_vera_scale(self.B_shared, self.b, self.d)
+            self.m.copy_(ops.dora_norm(self.W0, self.A_shared, Be, s).to(dt))
+        self.s = float(s)
+        self.flags = int(flags)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1]).contiguous()
+        y = DVoRAFunction.apply(x2, self.W0, self.A_shared, self.B_shared, self.b, self.d, self.m,
+                                self.s, self.flags)
         return y.reshape(*lead, y.shape[-1])

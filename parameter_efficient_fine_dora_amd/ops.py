@@ -185,6 +185,40 @@ def dora_merge(W0, A, B, m, s, *, norm=None, out=None, workspace=None):
     return out
 
 
+def dora_vera_scale(B_shared, b, d, *, out=None):
+    """DVoRA's effective B = diag(b) B_shared diag(d) ([d_out, r], layer dtype)."""
+    dev = B_shared.device
+    dt = B_shared.dtype
+    d_out, r = B_shared.shape
+    _need(b, "b", dt, (d_out,), dev)
+    _need(d, "d", dt, (r,), dev)
+    sh = _lib.shape(d_out, 8, r, 0, _layer_dtype(B_shared), 1.0)
+    if out is None:
+        out = torch.empty(d_out, r, dtype=dt, device=dev)
+    _need(out, "out", dt, (d_out, r), dev)
+    _check(_lib.lib().dora_vera_scale(ctypes.byref(sh), _ptr(B_shared), _ptr(b), _ptr(d), _ptr(out),
+                                      _stream(dev)), "dora_vera_scale")
+    return out
+
+
+def dora_vera_grads(grad_B_eff, B_shared, b, d, *, need=("b", "d"), workspace=None):
+    """DVoRA's vector gradients from grad_B_eff: returns (grad_b [d_out], grad_d [r])."""
+    dev = B_shared.device
+    dt = B_shared.dtype
+    d_out, r = B_shared.shape
+    _need(grad_B_eff, "grad_B_eff", dt, (d_out, r), dev)
+    _need(b, "b", dt, (d_out,), dev)
+    _need(d, "d", dt, (r,), dev)
+    sh = _lib.shape(d_out, 8, r, 0, _layer_dtype(B_shared), 1.0)
+    gb = torch.empty(d_out, dtype=dt, device=dev) if "b" in need else None
+    gd = torch.empty(r, dtype=dt, device=dev) if "d" in need else None
+    ws, nb = _ws(sh, _lib.OP_VERA_GRADS, dev, workspace)
+    _check(_lib.lib().dora_vera_grads(ctypes.byref(sh), _ptr(grad_B_eff), _ptr(B_shared), _ptr(b),
+                                      _ptr(d), _ptr(gb), _ptr(gd), _ptr(ws), nb, _stream(dev)),
+           "dora_vera_grads")
+    return gb, gd
+
+
 def timing_enable(on: bool = True):
     _lib.lib().dora_timing_enable(1 if on else 0)
 

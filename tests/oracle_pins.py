@@ -265,8 +265,79 @@ def pin_merged_weight(orc):
     _close(x @ Wm.T, y, 1e-13, "x W'_merged^T is the layer output")
 
 
+def _vera(seed, d_out=6, d_in=9, r=3, T=5):
+    rng = _rng(seed)
+    W0, A, B, m, x, gy = _layer(seed, d_out, d_in, r, T)
+    b = rng.normal(0.0, 1.0, d_out)
+    d = rng.normal(0.0, 1.0, r)
+    return W0, A, B, b, d, m, x, gy
+
+
+def pin_dvora_reduces_to_dora(orc):
+    """DVoRA is DoRA with B = diag(b) B_sh diag(d) ([DN] Sec. 3.5): the forward, and the
+    b, d gradients as the chain rule of DoRA's dB through that product."""
+    W0, A, B, b, d, m, x, gy = _vera(12)
+    s = 1.75
+    Be = b[:, None] * B * d[None, :]
+    y, n = orc.dvora_forward(x, W0, A, B, b, d, m, s)
+    y2, n2 = orc.dora_forward(x, W0, A, Be, m, s)
+    _close(n, n2, 1e-14, "DVoRA norm = DoRA norm with the effective B")
+    _close(y, y2, 1e-13, "DVoRA y = DoRA y with the effective B")
+    for exact in (False, True):
+        gv = orc.dvora_backward(gy, x, W0, A, B, b, d, m, s, exact=exact)
+        gd = orc.dora_backward(gy, x, W0, A, Be, m, s, exact=exact)
+        _close(gv["db"], np.sum(gd["dB"] * B * d[None, :], axis=1), 1e-13, "db from dB")
+        _close(gv["dd"], np.sum(gd["dB"] * B * b[:, None], axis=0), 1e-13, "dd from dB")
+        _close(gv["dx"], gd["dx"], 1e-13, "DVoRA dx")
+        _close(gv["dm"], gd["dm"], 1e-13, "DVoRA dm")
+    # b = 1, d = 1: plain DoRA with B = B_sh
+    y3, _ = orc.dvora_forward(x, W0, A, B, np.ones_like(b), np.ones_like(d), m, s)
+    y4, _ = orc.dora_forward(x, W0, A, B, m, s)
+    _close(y3, y4, 1e-13, "b = d = 1 is DoRA")
+
+
+def pin_dvora_vera_loops(orc):
+    """The VeRA product entry by entry: (Delta W)_ik = b_i sum_j B_ij d_j A_jk."""
+    _, A, B, b, d, _, _, _ = _vera(13)
+    dW = orc.vera_update(A, B, b, d)
+    for i in range(B.shape[0]):
+        for k in range(A.shape[1]):
+            v = b[i] * sum(B[i, j] * d[j] * A[j, k] for j in range(B.shape[1]))
+            assert abs(dW[i, k] - v) <= 1e-14 * max(1.0, abs(v)), (i, k)
+
+
+def pin_dvora_fd(orc):
+    """Central finite differences of L = sum(gy * y) in b and d, norm detached and exact."""
+    W0, A, B, b, d, m, x, gy = _vera(14, d_out=4, d_in=5, r=2, T=3)
+    s = 0.9
+    for exact in (False, True):
+        gr = orc.dvora_backward(gy, x, W0, A, B, b, d, m, s, exact=exact)
+        for name, vec in (("db", b), ("dd", d)):
+            num = np.zeros_like(vec)
+            for k in range(vec.size):
+                h = 1e-6
+                vp, vm = vec.copy(), vec.copy()
+                vp[k] += h
+                vm[k] -= h
+                args_p = (vp, d) if name == "db" else (b, vp)
+                args_m = (vm, d) if name == "db" else (b, vm)
+                if exact:
+                    Lp = np.sum(gy * orc.dvora_forward(x, W0, A, B, *args_p, m, s)[0])
+                    Lm = np.sum(gy * orc.dvora_forward(x, W0, A, B, *args_m, m, s)[0])
+                else:   # detached: the norm is held at its value at the base point
+                    n0 = orc.dvora_forward(x, W0, A, B, b, d, m, s)[1]
+                    def y_frozen(bb, dd):
+                        V = W0 + s * orc.vera_update(A, B, bb, dd)
+                        return x @ ((m / np.maximum(n0, 1e-8))[:, None] * V).T
+                    Lp = np.sum(gy * y_frozen(*args_p))
+                    Lm = np.sum(gy * y_frozen(*args_m))
+                num[k] = (Lp - Lm) / (2 * h)
+            _close(gr[name], num, 1e-6, f"FD {name} exact={exact}")
+
+
 ALL_PINS = [
     pin_worked_rows, pin_bruteforce, pin_factored_identity, pin_b_zero, pin_g_one_is_lora,
     pin_scale_invariance, pin_s_zero_weightnorm, pin_token_permutation, pin_fd_detached,
     pin_fd_exact, pin_eq8_closed_form, pin_b_zero_backward, pin_sampled_forms, pin_merged_weight,
+    pin_dvora_reduces_to_dora, pin_dvora_vera_loops, pin_dvora_fd,
 ]

@@ -21,7 +21,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     names = set(declared_symbols())
-    assert {"dora_norm", "dora_forward", "dora_backward", "dora_merge", "dora_workspace_bytes",
+    assert {"dora_norm", "dora_forward", "dora_backward", "dora_merge", "dora_vera_scale",
+            "dora_vera_grads", "dora_workspace_bytes",
             "dora_strerror", "dora_timing_enable", "dora_timing_collect"} <= names
 
 
@@ -109,6 +110,25 @@ def test_merge_validation():
     big = _lib.shape(8192, 8192, 384, 0, _lib.BF16, 2.0)
     assert (_lib.workspace_bytes(big, _lib.OP_MERGE) - _lib.workspace_bytes(big, _lib.OP_NORM)
             <= 8192 * 4 + 1024)
+
+
+def test_vera_validation():
+    """dora_vera_scale / dora_vera_grads: required tensors, optional outputs, workspace."""
+    L = _lib.lib()
+    sh = _lib.shape(64, 64, 8, 0, _lib.BF16, 1.0)
+    assert L.dora_vera_scale(ctypes.byref(sh), FAKE, FAKE, FAKE, None, None) == _lib.ERR_CODE["DORA_ERR_NULL"]
+    assert L.dora_vera_scale(ctypes.byref(sh), FAKE, None, FAKE, FAKE, None) == _lib.ERR_CODE["DORA_ERR_NULL"]
+    assert L.dora_vera_scale(ctypes.byref(sh), FAKE, FAKE, FAKE + 2, FAKE, None) == _lib.ERR_CODE["DORA_ERR_ALIGN"]
+    need = _lib.workspace_bytes(sh, _lib.OP_VERA_GRADS)
+    assert 0 < need <= 64 * 8 * 4 + 1024
+
+    def grads(gBe=FAKE, Bsh=FAKE, b=FAKE, d=FAKE, gb=FAKE, gd=FAKE, ws=FAKE, nb=need):
+        return L.dora_vera_grads(ctypes.byref(sh), gBe, Bsh, b, d, gb, gd, ws, nb, None)
+
+    for kw in ("gBe", "Bsh", "b", "d", "ws"):
+        assert grads(**{kw: None}) == _lib.ERR_CODE["DORA_ERR_NULL"], kw
+    assert grads(nb=need - 1) == _lib.ERR_CODE["DORA_ERR_WORKSPACE"]
+    assert grads(gd=FAKE + 4) == _lib.ERR_CODE["DORA_ERR_ALIGN"]
 
 
 def test_exact_flag_needs_its_own_workspace():

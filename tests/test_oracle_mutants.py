@@ -37,6 +37,11 @@ MUTANTS = {
                       "    g = magnitude_scale(m, row_norms(V))\n    return V"),
     "merge_scales_columns": ("    g = magnitude_scale(m, row_norms(V))\n    return g[:, None] * V",
                              "    g = magnitude_scale(m, row_norms(V))\n    return V * np.resize(g, V.shape[1])[None, :]"),
+    "vera_drops_d": ("return np.diag(_f64(b)) @ _f64(B_sh) @ np.diag(_f64(d)) @ _f64(A_sh)",
+                     "return np.diag(_f64(b)) @ _f64(B_sh) @ _f64(A_sh)"),
+    "dvora_dd_drops_b": ('dd = s * np.einsum("ik,i,ij,jk->j", dV, b, B_sh, A_sh)',
+                         'dd = s * np.einsum("ik,ij,jk->j", dV, B_sh, A_sh)'),
+    "dvora_db_drops_d": ("BdA = B_sh @ np.diag(d) @ A_sh", "BdA = B_sh @ A_sh"),
     "sampled_rows_use_first_rows": ("V = _f64(W0[rows]) + float(s) * (_f64(B[rows]) @ _f64(A))\n    return row_norms(V)",
                                     "V = _f64(W0[:len(rows)]) + float(s) * (_f64(B[:len(rows)]) @ _f64(A))\n    return row_norms(V)"),
 }
