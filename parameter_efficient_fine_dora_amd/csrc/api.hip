@@ -78,12 +78,16 @@ int64_t p_depth(const dora_shape& s) { return s.d_in + (s.dtype == kBF16 ? 2 : 1
 int gram_splits(const dora_shape& s) {
   return s.r > 0 ? plan_gemm(s.r, s.r, s.d_in, s.dtype).split : 1;
 }
+// bf16 layers with a rank take ||W0_i||^2 from the projection's own pass over W0.
+bool fused_rowsq(const dora_shape& s) { return s.dtype == kBF16 && s.r > 0; }
+
 int p_splits(const dora_shape& s) {
   return s.r > 0 ? plan_gemm(s.d_out, s.r, p_depth(s), s.dtype).split : 1;
 }
 
 struct Layout {
   size_t gpart = 0, ghi = 0, glo = 0, P = 0;     // norm
+  size_t rowsq = 0;                              // norm: partial ||W0_i||^2 of the projection
   size_t xs = 0, slora = 0;                      // forward
   size_t gz = 0, ts = 0, dmpart = 0;             // backward
   size_t mnorm = 0;                              // merge: the row norms when not given
@@ -120,6 +124,7 @@ Layout layout(const dora_shape& s, int op) {
     L.ghi = take(r * r * (s.dtype == kBF16 ? 2 : 4));
     L.glo = take(s.dtype == kBF16 ? r * r * 2 : 0);
     L.P = take((size_t)L.psplits * s.d_out * r * 4);
+    if (fused_rowsq(s)) L.rowsq = take((size_t)L.psplits * s.d_out * 4);
   }
   if (op == DORA_OP_VERA_GRADS) L.vpart = take((size_t)vera_dd_blocks(s.d_out) * r * 4);
   if (op == DORA_OP_MERGE) {
@@ -216,11 +221,13 @@ void give_scratch(GemmProblem& g, void* ws, const Layout& L) {
 }
 
 // Factored norm: G = A A^T (split-K), (s/2) G -> hi/lo, P = 2s W0 A^T + s^2 B G,
-// n_i = sqrt(||W0_i||^2 + B_i . P_i).
+// n_i = sqrt(||W0_i||^2 + B_i . P_i); for bf16 the projection also sums the
+// squares of the W0 rows it streams, so W0 is read once.
 int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, float* norm,
              void* ws, const Layout& L, hipStream_t st) {
   const int dt = s.dtype;
   float* P = nullptr;
+  float* rowsq = nullptr;
   if (s.r > 0) {
     float* gpart = reinterpret_cast<float*>(at(ws, L.gpart));
     void* ghi = at(ws, L.ghi);
@@ -256,9 +263,14 @@ int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, 
     p.split = L.psplits;
     p.split_stride = s.d_out * s.r;
     p.cfg = plan_gemm(s.d_out, s.r, p_depth(s), dt).cfg;
+    if (fused_rowsq(s)) {
+      rowsq = reinterpret_cast<float*>(at(ws, L.rowsq));
+      p.epi = kEpiRowSq;
+      p.rowsq = rowsq;
+    }
     HIP_TRY(gemm(p, dt, st, "cross_gram_proj"));
   }
-  HIP_TRY(row_norm(W0, B, P, L.psplits, norm, s.d_out, s.d_in, s.r, dt, st));
+  HIP_TRY(row_norm(W0, B, P, rowsq, L.psplits, norm, s.d_out, s.d_in, s.r, dt, st));
   return DORA_OK;
 }
 

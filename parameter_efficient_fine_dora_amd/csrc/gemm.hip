@@ -59,6 +59,7 @@ struct KArgs {
   const float* norm;
   const void* add;
   int64_t ld_add;
+  float* rowsq;          // kEpiRowSq: [gridDim.y, M] sums of squares of opA over segment 0
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
@@ -452,6 +453,12 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  constexpr bool kRowSq = EPI == kEpiRowSq;
+  const bool sq_wave = kRowSq && wn == 0 && tc.y == 0;
+  float sq[2][MB];   // kEpiRowSq: per-lane partial sums of squares of the lane's opA rows
+#pragma unroll
+  for (int i = 0; i < MB; ++i) sq[0][i] = sq[1][i] = 0.f;
+
   // Fragment read bases: the swizzle of row wm*TM + i*32 + lane%32 depends on i
   // only through its parity, and the chunk of step kk only through an XOR.
   uint32_t ra[2][4], rb[2][4];
@@ -500,7 +507,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
                                          (SB) * BBYTES);                                   \
   } while (0)
   // One stage: four 16-deep steps, fragments of step kk+1 read during step kk.
-#define DORA_MMA(SB)                                                                       \
+#define DORA_MMA(SB, SQ)                                                                   \
   do {                                                                                     \
     DORA_READ(0, SB, 0);                                                                   \
     _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                     \
@@ -514,6 +521,15 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][j], af[kk & 1][i],      \
                                                       acc[i][j], 0, 0, 0);                 \
       __builtin_amdgcn_sched_barrier(0);                                                   \
+      if (SQ) {                                                                            \
+        _Pragma("unroll") for (int i = 0; i < MB; ++i)                                     \
+            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                \
+          /* the pair is built from elements: a bit_cast of a vector element */            \
+          /* (w[q]) compiles to a read of element 0 with this clang          */            \
+          const bf16x2 h_ = {af[kk & 1][i][2 * q], af[kk & 1][i][2 * q + 1]};              \
+          sq[kk & 1][i] = __builtin_amdgcn_fdot2_f32_bf16(h_, h_, sq[kk & 1][i], false);   \
+        }                                                                                  \
+      }                                                                                    \
     }                                                                                      \
   } while (0)
 
@@ -540,24 +556,45 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
     DORA_COMMIT(0);
     wait_vmem();
     barrier_nofence();
-    for (int kr = r_lo; kr < r_hi; kr += 2) {
-      if (kr + 1 < r_hi) DORA_FETCH(kr + 1, 1);
-      DORA_MMA(0);
-      if (kr + 1 < r_hi) DORA_COMMIT(1);
-      wait_vmem();
-      barrier_nofence();
-      if (kr + 1 >= r_hi) break;
-      if (kr + 2 < r_hi) DORA_FETCH(kr + 2, 0);
-      DORA_MMA(1);
-      if (kr + 2 < r_hi) DORA_COMMIT(0);
-      wait_vmem();
-      barrier_nofence();
-    }
+#define DORA_STAGES(SQ)                                                                    \
+  for (int kr = r_lo; kr < r_hi; kr += 2) {                                                \
+    if (kr + 1 < r_hi) DORA_FETCH(kr + 1, 1);                                              \
+    DORA_MMA(0, SQ);                                                                       \
+    if (kr + 1 < r_hi) DORA_COMMIT(1);                                                     \
+    wait_vmem();                                                                           \
+    barrier_nofence();                                                                     \
+    if (kr + 1 >= r_hi) break;                                                             \
+    if (kr + 2 < r_hi) DORA_FETCH(kr + 2, 0);                                              \
+    DORA_MMA(1, SQ);                                                                       \
+    if (kr + 2 < r_hi) DORA_COMMIT(0);                                                     \
+    wait_vmem();                                                                           \
+    barrier_nofence();                                                                     \
   }
+    // Row sums of squares ride on the segment-0 fragments that the first
+    // column of waves of the first column of tiles already holds (a
+    // wave-uniform flag; a loop copy per case would double the live registers).
+    const bool sq_now = kRowSq && seg == 0 && sq_wave;
+    DORA_STAGES(sq_now)
+  }
+#undef DORA_STAGES
 #undef DORA_FETCH
 #undef DORA_COMMIT
 #undef DORA_READ
 #undef DORA_MMA
+
+  if constexpr (kRowSq) {
+    // Lane l and lane l + 32 hold the two halves of every 16-deep step of
+    // one row; each split writes its partial (zero if it saw no segment-0 step).
+    if (sq_wave) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        float v = sq[0][i] + sq[1][i];
+        v += __shfl_xor(v, 32);
+        const int m = m0 + wm * TM + i * 32 + lane;
+        if (lane < 32 && m < M) p.rowsq[(int64_t)blockIdx.y * M + m] = v;
+      }
+    }
+  }
 
   gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, smem, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
                                                 p.norm, p.add, p.ld_add, M, N, m0, n0, wave, wm,
@@ -682,6 +719,14 @@ template <int BM, int BN, int WM, int WN, bool AKC, bool BKC>
 hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStream_t st) {
   const dim3 block(WM * WN * 64);
   if (out_f32) {
+    if constexpr (AKC && BKC) {   // row sums of squares of a K-contiguous opA (the norm's W0)
+      if (epi == kEpiRowSq) {
+        hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiRowSq, true>), grid,
+                           block, 0, st, a);
+        return hipGetLastError();
+      }
+    }
+    if (epi == kEpiRowSq) return hipErrorInvalidValue;
     hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, true>), grid, block, 0,
                        st, a);
     return hipGetLastError();
@@ -780,6 +825,7 @@ int fill_args(const GemmProblem& p, KArgs& a) {
   a.norm = p.norm;
   a.add = p.add;
   a.ld_add = p.ld_add;
+  a.rowsq = p.rowsq;
   return kt;
 }
 
@@ -828,6 +874,10 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
   int64_t K = 0;
   for (int s = 0; s < p.nseg; ++s) K += p.seg[s].K > 0 ? p.seg[s].K : 0;
 
+  if (p.epi == kEpiRowSq &&
+      (dtype != kBF16 || !p.out_f32 || !p.a_kcontig || !p.b_kcontig || !p.rowsq || p.nseg < 1 ||
+       p.seg[0].K <= 0))
+    return hipErrorInvalidValue;
   if (dtype == kF32) {
     LaunchTimer timer(label, st);
     a.tiles_m = (int)cdiv64(p.M, 64);

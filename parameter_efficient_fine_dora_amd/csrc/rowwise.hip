@@ -85,13 +85,16 @@ __global__ __launch_bounds__(256) void dora_gram_finalize(const float* part, int
 // go straight to registers) and the lane partials meet in a wave reduction.
 template <bool BF>
 __global__ __launch_bounds__(256) void dora_row_norm(const void* W0, const void* B, const float* P,
-                                                     int p_splits, int64_t p_stride, float* norm,
+                                                     const float* rowsq, int p_splits,
+                                                     int64_t p_stride, float* norm,
                                                      int64_t d_out, int64_t d_in, int64_t r) {
   using V = Vec<BF>;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= d_out) return;   // whole wave leaves; the kernel has no barrier
-  const int64_t nv = d_in / V::kN;
+  // ||W0_i||^2: from the projection's partial row sums of squares when given
+  // (then W0 is not read again), else streamed from W0.
+  const int64_t nv = rowsq ? 0 : d_in / V::kN;
   const int64_t wbase = row * nv;
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
   int64_t c = lane;
@@ -132,6 +135,8 @@ __global__ __launch_bounds__(256) void dora_row_norm(const void* W0, const void*
       acc1 = fmaf(bv[q + 3], pv[3], acc1);
     }
   }
+  if (rowsq)
+    for (int z = lane; z < p_splits; z += 64) acc2 += rowsq[(int64_t)z * d_out + row];
   const float tot = wave_sum((acc0 + acc1) + (acc2 + acc3));
   if (lane == 0) norm[row] = sqrtf(fmaxf(tot, 0.f));
 }
@@ -473,18 +478,18 @@ hipError_t db_combine(const float* d1, int d1_splits, const float* q, int q_spli
   return hipGetLastError();
 }
 
-hipError_t row_norm(const void* W0, const void* B, const float* P, int p_splits,
-                    float* norm, int64_t d_out, int64_t d_in, int64_t r, int dtype,
+hipError_t row_norm(const void* W0, const void* B, const float* P, const float* rowsq,
+                    int p_splits, float* norm, int64_t d_out, int64_t d_in, int64_t r, int dtype,
                     hipStream_t st) {
   LaunchTimer t("row_norm", st);
   const dim3 grid((unsigned)cdiv(d_out, 4));
   const int64_t stride = d_out * r;
   if (dtype == kBF16)
-    hipLaunchKernelGGL(dora_row_norm<true>, grid, dim3(256), 0, st, W0, B, P, p_splits, stride,
-                       norm, d_out, d_in, r);
+    hipLaunchKernelGGL(dora_row_norm<true>, grid, dim3(256), 0, st, W0, B, P, rowsq, p_splits,
+                       stride, norm, d_out, d_in, r);
   else
-    hipLaunchKernelGGL(dora_row_norm<false>, grid, dim3(256), 0, st, W0, B, P, p_splits, stride,
-                       norm, d_out, d_in, r);
+    hipLaunchKernelGGL(dora_row_norm<false>, grid, dim3(256), 0, st, W0, B, P, rowsq, p_splits,
+                       stride, norm, d_out, d_in, r);
   return hipGetLastError();
 }
 

@@ -263,6 +263,39 @@ def test_norm_terms_separately(ops):
     check_norm(n0, np.sqrt(base), "B = 0 norm", rtol=1e-5)
 
 
+# ---- ||W0_i||^2 summed inside the cross/Gram projection -----------------------------
+
+PROJ = [
+    # 128 x 128 tiles, two K splits, the second of which sees no W0 step
+    ("split_without_W0", LayerShape(1024, 64, 512, 0, 2.0, "bf16"), 21),
+    # a partial 64-deep W0 step (d_in = 72) and a ragged last row tile
+    ("ragged_W0_tail", LayerShape(1000, 72, 520, 0, 2.0, "bf16"), 22),
+    # 256 x 128 tiles with four wave rows
+    ("tiles_256x128", LayerShape(8192, 256, 1024, 0, 2.0, "bf16"), 23),
+    # 256 x 256 tiles
+    ("tiles_256x256", LayerShape(16384, 128, 4096, 0, 2.0, "bf16"), 24),
+]
+
+
+@pytest.mark.parametrize("name,shape,seed", PROJ, ids=[c[0] for c in PROJ])
+def test_norm_projection_row_squares(ops, name, shape, seed):
+    """Row norms when the base term comes from the projection's pass over W0,
+    over the tile shapes and K splits the projection can take."""
+    say(f"norm via projection row squares {name} shape={shape}")
+    layer = synth.make_layer(shape, seed, b_std=0.05)
+    dev = layer_to_device(layer, "bf16")
+    n = download(ops.dora_norm(dev["W0"], dev["A"], dev["B"], shape.s))
+    L = synth.layer_f64(layer, "bf16")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = np.unique(np.concatenate([_sample(rng, shape.d_out, 512),
+                                     np.arange(shape.d_out - 8, shape.d_out)]))
+    n_ref = oracle.dora_norm(L["W0"][rows], L["A"], L["B"][rows], shape.s)
+    check_norm(n[rows], n_ref, f"{name} norm (sampled rows)")
+    # B = 0: the norm is ||W0_i|| alone
+    n0 = download(ops.dora_norm(dev["W0"], dev["A"], torch.zeros_like(dev["B"]), shape.s))
+    check_norm(n0[rows], np.linalg.norm(L["W0"][rows], axis=1), f"{name} B = 0 norm", rtol=1e-5)
+
+
 # ---- near-unity rescaling (float32 storage, so the output can show it) ---------------
 
 def test_near_unity_compose_f32(ops):
