@@ -72,8 +72,9 @@ def algorithmic_work(d_out, d_in, r, T):
     return {
         "gram_AAt": ("flop", 2 * r * r * d_in),
         "cross_gram_proj": ("flop", 2 * d_out * r * d_in + 2 * d_out * r * r),
-        # ||W0_i||^2 arrives from the projection's pass over W0 (one float per row)
-        "row_norm": ("byte", d_out * r * e + d_out * r * 4 + d_out * 4 + d_out * 4),
+        # the projection hands over per-row partials; their count is a tiling
+        # detail, so the finalize counts one float in and one out per row
+        "norm_finalize": ("byte", d_out * 4 + d_out * 4),
         "down_proj_xs": ("flop", 2 * T * r * d_in),
         "fused_fwd_gemm": ("flop", 2 * T * d_out * (d_in + r)),
         "base_gemm": ("flop", 2 * T * d_out * d_in),

@@ -78,8 +78,11 @@ int64_t p_depth(const dora_shape& s) { return s.d_in + (s.dtype == kBF16 ? 2 : 1
 int gram_splits(const dora_shape& s) {
   return s.r > 0 ? plan_gemm(s.r, s.r, s.d_in, s.dtype).split : 1;
 }
-// bf16 layers with a rank take ||W0_i||^2 from the projection's own pass over W0.
-bool fused_rowsq(const dora_shape& s) { return s.dtype == kBF16 && s.r > 0; }
+// bf16 layers with a rank reduce the projection to per-row partials inside it
+// (||W0_i||^2 from its pass over W0, B_i . P_i from its accumulators); P
+// itself is never stored.
+bool fused_norm(const dora_shape& s) { return s.dtype == kBF16 && s.r > 0; }
+int p_cfg(const dora_shape& s) { return plan_gemm(s.d_out, s.r, p_depth(s), s.dtype).cfg; }
 
 int p_splits(const dora_shape& s) {
   return s.r > 0 ? plan_gemm(s.d_out, s.r, p_depth(s), s.dtype).split : 1;
@@ -87,7 +90,8 @@ int p_splits(const dora_shape& s) {
 
 struct Layout {
   size_t gpart = 0, ghi = 0, glo = 0, P = 0;     // norm
-  size_t rowsq = 0;                              // norm: partial ||W0_i||^2 of the projection
+  size_t rowsq = 0, rowdot = 0;                  // norm: the projection's per-row partials
+  int64_t dot_parts = 0;
   size_t xs = 0, slora = 0;                      // forward
   size_t gz = 0, ts = 0, dmpart = 0;             // backward
   size_t mnorm = 0;                              // merge: the row norms when not given
@@ -123,8 +127,13 @@ Layout layout(const dora_shape& s, int op) {
     L.gpart = take((size_t)L.splits * r * r * 4);
     L.ghi = take(r * r * (s.dtype == kBF16 ? 2 : 4));
     L.glo = take(s.dtype == kBF16 ? r * r * 2 : 0);
-    L.P = take((size_t)L.psplits * s.d_out * r * 4);
-    if (fused_rowsq(s)) L.rowsq = take((size_t)L.psplits * s.d_out * 4);
+    if (fused_norm(s)) {
+      L.dot_parts = L.psplits * gemm_col_slots(p_cfg(s), s.r);
+      L.rowsq = take((size_t)L.psplits * s.d_out * 4);
+      L.rowdot = take((size_t)L.dot_parts * s.d_out * 4);
+    } else {
+      L.P = take((size_t)L.psplits * s.d_out * r * 4);
+    }
   }
   if (op == DORA_OP_VERA_GRADS) L.vpart = take((size_t)vera_dd_blocks(s.d_out) * r * 4);
   if (op == DORA_OP_MERGE) {
@@ -221,56 +230,64 @@ void give_scratch(GemmProblem& g, void* ws, const Layout& L) {
 }
 
 // Factored norm: G = A A^T (split-K), (s/2) G -> hi/lo, P = 2s W0 A^T + s^2 B G,
-// n_i = sqrt(||W0_i||^2 + B_i . P_i); for bf16 the projection also sums the
-// squares of the W0 rows it streams, so W0 is read once.
+// n_i = sqrt(||W0_i||^2 + B_i . P_i).  For bf16 the projection itself reduces
+// each row: it sums the squares of the W0 rows it streams and dots its
+// accumulators with B, so W0 crosses HBM once and P never reaches it.
 int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, float* norm,
              void* ws, const Layout& L, hipStream_t st) {
   const int dt = s.dtype;
-  float* P = nullptr;
-  float* rowsq = nullptr;
-  if (s.r > 0) {
-    float* gpart = reinterpret_cast<float*>(at(ws, L.gpart));
-    void* ghi = at(ws, L.ghi);
-    void* glo = at(ws, L.glo);
-    P = reinterpret_cast<float*>(at(ws, L.P));
-    GemmProblem g;
-    g.M = g.N = s.r;
-    g.nseg = 1;
-    g.seg[0] = {A, A, s.d_in, s.d_in, s.d_in};
-    g.c = gpart;
-    g.ldc = s.r;
-    g.out_f32 = true;
-    g.split = L.splits;
-    g.split_stride = s.r * s.r;
-    g.cfg = plan_gemm(s.r, s.r, s.d_in, dt).cfg;
-    HIP_TRY(gemm(g, dt, st, "gram_AAt"));
-    HIP_TRY(gram_finalize(gpart, L.splits, s.r, 0.5f * s.s, dt, ghi, glo, st, "gram_finalize"));
-
-    GemmProblem p;
-    p.M = s.d_out;
-    p.N = s.r;
-    p.seg[0] = {W0, A, s.d_in, s.d_in, s.d_in};
-    p.seg[1] = {B, ghi, s.r, s.r, s.r};
-    p.nseg = 2;
-    if (dt == kBF16) {
-      p.seg[2] = {B, glo, s.r, s.r, s.r};
-      p.nseg = 3;
-    }
-    p.alpha = 2.f * s.s;
-    p.c = P;
-    p.ldc = s.r;
-    p.out_f32 = true;
-    p.split = L.psplits;
-    p.split_stride = s.d_out * s.r;
-    p.cfg = plan_gemm(s.d_out, s.r, p_depth(s), dt).cfg;
-    if (fused_rowsq(s)) {
-      rowsq = reinterpret_cast<float*>(at(ws, L.rowsq));
-      p.epi = kEpiRowSq;
-      p.rowsq = rowsq;
-    }
-    HIP_TRY(gemm(p, dt, st, "cross_gram_proj"));
+  if (s.r == 0) {
+    HIP_TRY(row_norm(W0, B, nullptr, L.psplits, norm, s.d_out, s.d_in, s.r, dt, st));
+    return DORA_OK;
   }
-  HIP_TRY(row_norm(W0, B, P, rowsq, L.psplits, norm, s.d_out, s.d_in, s.r, dt, st));
+  float* gpart = reinterpret_cast<float*>(at(ws, L.gpart));
+  void* ghi = at(ws, L.ghi);
+  void* glo = at(ws, L.glo);
+  GemmProblem g;
+  g.M = g.N = s.r;
+  g.nseg = 1;
+  g.seg[0] = {A, A, s.d_in, s.d_in, s.d_in};
+  g.c = gpart;
+  g.ldc = s.r;
+  g.out_f32 = true;
+  g.split = L.splits;
+  g.split_stride = s.r * s.r;
+  g.cfg = plan_gemm(s.r, s.r, s.d_in, dt).cfg;
+  HIP_TRY(gemm(g, dt, st, "gram_AAt"));
+  HIP_TRY(gram_finalize(gpart, L.splits, s.r, 0.5f * s.s, dt, ghi, glo, st, "gram_finalize"));
+
+  GemmProblem p;
+  p.M = s.d_out;
+  p.N = s.r;
+  p.seg[0] = {W0, A, s.d_in, s.d_in, s.d_in};
+  p.seg[1] = {B, ghi, s.r, s.r, s.r};
+  p.nseg = 2;
+  if (dt == kBF16) {
+    p.seg[2] = {B, glo, s.r, s.r, s.r};
+    p.nseg = 3;
+  }
+  p.alpha = 2.f * s.s;
+  p.out_f32 = true;
+  p.split = L.psplits;
+  p.cfg = p_cfg(s);
+  if (fused_norm(s)) {
+    float* rowsq = reinterpret_cast<float*>(at(ws, L.rowsq));
+    float* rowdot = reinterpret_cast<float*>(at(ws, L.rowdot));
+    p.epi = kEpiNorm;
+    p.rowsq = rowsq;
+    p.rowdot = rowdot;
+    p.add = B;
+    p.ld_add = s.r;
+    HIP_TRY(gemm(p, dt, st, "cross_gram_proj"));
+    HIP_TRY(norm_finalize(rowsq, L.psplits, rowdot, L.dot_parts, norm, s.d_out, st));
+    return DORA_OK;
+  }
+  float* P = reinterpret_cast<float*>(at(ws, L.P));
+  p.c = P;
+  p.ldc = s.r;
+  p.split_stride = s.d_out * s.r;
+  HIP_TRY(gemm(p, dt, st, "cross_gram_proj"));
+  HIP_TRY(row_norm(W0, B, P, L.psplits, norm, s.d_out, s.d_in, s.r, dt, st));
   return DORA_OK;
 }
 

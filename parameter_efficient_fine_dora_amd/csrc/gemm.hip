@@ -59,7 +59,8 @@ struct KArgs {
   const float* norm;
   const void* add;
   int64_t ld_add;
-  float* rowsq;          // kEpiRowSq: [gridDim.y, M] sums of squares of opA over segment 0
+  float* rowsq;          // kEpiNorm: [gridDim.y][M] sums of squares of opA over segment 0
+  float* rowdot;         // kEpiNorm: [gridDim.y][tiles_n][WN][M] row dots of alpha*C with `add`
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
@@ -453,9 +454,9 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  constexpr bool kRowSq = EPI == kEpiRowSq;
+  constexpr bool kRowSq = EPI == kEpiNorm;
   const bool sq_wave = kRowSq && wn == 0 && tc.y == 0;
-  float sq[2][MB];   // kEpiRowSq: per-lane partial sums of squares of the lane's opA rows
+  float sq[2][MB];   // kEpiNorm: per-lane partial sums of squares of the lane's opA rows
 #pragma unroll
   for (int i = 0; i < MB; ++i) sq[0][i] = sq[1][i] = 0.f;
 
@@ -594,6 +595,40 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
         if (lane < 32 && m < M) p.rowsq[(int64_t)blockIdx.y * M + m] = v;
       }
     }
+    // C itself is not stored: each lane dots its accumulators with the rows
+    // of `add` at the same (m, n) (in-lane over j, g, e, then the two lanes
+    // that share a row), one partial per split, column tile and wave column.
+    const uint16_t* addp = reinterpret_cast<const uint16_t*>(p.add);
+    float dot[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) dot[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
+        if (n >= N) continue;   // N % 4 == 0: n < N covers n..n+3
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int m = m0 + wm * TM + i * 32 + (lane & 31);
+          if (m >= M) continue;
+          const u32x2 w = *reinterpret_cast<const u32x2*>(addp + (int64_t)m * p.ld_add + n);
+          dot[i] = fmaf(bf_lo(w[0]), acc[i][j][g * 4 + 0], dot[i]);
+          dot[i] = fmaf(bf_hi(w[0]), acc[i][j][g * 4 + 1], dot[i]);
+          dot[i] = fmaf(bf_lo(w[1]), acc[i][j][g * 4 + 2], dot[i]);
+          dot[i] = fmaf(bf_hi(w[1]), acc[i][j][g * 4 + 3], dot[i]);
+        }
+      }
+    }
+    const int64_t slot = ((int64_t)blockIdx.y * p.tiles_n + tc.y) * WN + wn;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      float v = dot[i];
+      v += __shfl_xor(v, 32);
+      const int m = m0 + wm * TM + i * 32 + lane;
+      if (lane < 32 && m < M) p.rowdot[slot * M + m] = p.alpha * v;
+    }
+    return;
   }
 
   gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, smem, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
@@ -687,10 +722,16 @@ __global__ __launch_bounds__(256) void dora_splitk_reduce(const float* part, int
                                                           int out_bf16) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
-  f32x4 acc = reinterpret_cast<const f32x4*>(part)[i];
-  for (int z = 1; z < S; ++z) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(part + z * stride)[i];
-    acc += v;
+  // partials added in index order, their loads issued four at a time
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < S; z0 += 4) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (z0 + u < S) v[u] = reinterpret_cast<const f32x4*>(part + (z0 + u) * stride)[i];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (z0 + u < S) acc = (z0 + u == 0) ? v[u] : acc + v[u];
   }
   acc *= alpha;
   if (out_bf16)
@@ -719,14 +760,14 @@ template <int BM, int BN, int WM, int WN, bool AKC, bool BKC>
 hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStream_t st) {
   const dim3 block(WM * WN * 64);
   if (out_f32) {
-    if constexpr (AKC && BKC) {   // row sums of squares of a K-contiguous opA (the norm's W0)
-      if (epi == kEpiRowSq) {
-        hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiRowSq, true>), grid,
+    if constexpr (AKC && BKC) {   // the norm's projection: W0 and A are K-contiguous
+      if (epi == kEpiNorm) {
+        hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiNorm, true>), grid,
                            block, 0, st, a);
         return hipGetLastError();
       }
     }
-    if (epi == kEpiRowSq) return hipErrorInvalidValue;
+    if (epi == kEpiNorm) return hipErrorInvalidValue;
     hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, true>), grid, block, 0,
                        st, a);
     return hipGetLastError();
@@ -826,6 +867,7 @@ int fill_args(const GemmProblem& p, KArgs& a) {
   a.add = p.add;
   a.ld_add = p.ld_add;
   a.rowsq = p.rowsq;
+  a.rowdot = p.rowdot;
   return kt;
 }
 
@@ -862,6 +904,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bk
   return {cfg, (int)split};
 }
 
+int64_t gemm_col_slots(int cfg, int64_t N) {
+  if (cfg < 0 || cfg >= kNumCfgs) return 0;
+  return cdiv64(N, kCfgs[cfg].bn) * kCfgs[cfg].wn;
+}
+
 size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bkc) {
   const GemmPlan pl = plan_gemm(M, N, K, dtype, akc, bkc);
   return pl.split > 1 ? (size_t)pl.split * M * N * 4 : 0;
@@ -874,9 +921,9 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
   int64_t K = 0;
   for (int s = 0; s < p.nseg; ++s) K += p.seg[s].K > 0 ? p.seg[s].K : 0;
 
-  if (p.epi == kEpiRowSq &&
-      (dtype != kBF16 || !p.out_f32 || !p.a_kcontig || !p.b_kcontig || !p.rowsq || p.nseg < 1 ||
-       p.seg[0].K <= 0))
+  if (p.epi == kEpiNorm &&
+      (dtype != kBF16 || !p.out_f32 || !p.a_kcontig || !p.b_kcontig || !p.rowsq || !p.rowdot ||
+       !p.add || p.N % 4 != 0 || p.nseg < 1 || p.seg[0].K <= 0))
     return hipErrorInvalidValue;
   if (dtype == kF32) {
     LaunchTimer timer(label, st);

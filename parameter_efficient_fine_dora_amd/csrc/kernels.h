@@ -21,8 +21,9 @@ enum Epilogue : int {
   kEpiStore = 0,     // C = alpha * acc
   kEpiCompose = 1,   // C = z + (g - 1) z with z = alpha * acc, g_n = m_n / max(norm_n, eps)
   kEpiMerge = 2,     // C = g_m (add + alpha * acc) with g_m = m_m / max(norm_m, eps) per ROW
-  kEpiRowSq = 3,     // C = alpha * acc (float32) and rowsq[z, m] = sum over segment 0 of opA(m, k)^2
-                     // (bf16, both operands K-contiguous; z = split index)
+  kEpiNorm = 3,      // C is not stored; rowsq[z][m] = sum over segment 0 of opA(m, k)^2 and
+                     // rowdot[z][tile_n][wave column][m] = alpha * sum over the tile's n of
+                     // C(m, n) * add(m, n) (bf16, both operands K-contiguous; z = split index)
 };
 
 struct GemmProblem {
@@ -41,7 +42,8 @@ struct GemmProblem {
   const float* norm = nullptr; // kEpiCompose: n [N]; kEpiMerge: n [M] (float32)
   const void* add = nullptr;   // kEpiMerge: addend [M, N] (layer dtype), row stride ld_add
   int64_t ld_add = 0;
-  float* rowsq = nullptr;      // kEpiRowSq: [split][M] float32 partial row sums of squares
+  float* rowsq = nullptr;      // kEpiNorm: [split][M] float32 partial row sums of squares
+  float* rowdot = nullptr;     // kEpiNorm: [gemm_col_slots * split][M] float32 partial row dots
   // Library-chosen split-K (layer-dtype store epilogue only): float32 partial
   // sums go to `scratch`, then a fixed-order reduction writes C.
   void* scratch = nullptr;
@@ -58,6 +60,9 @@ struct GemmPlan {
 // Tile configuration and split-K factor for a layer-dtype GEMM of this size
 // and operand layout.
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc = true, bool bkc = true);
+
+// Row-dot partials per split of a kEpiNorm GEMM with N columns on tile configuration cfg.
+int64_t gemm_col_slots(int cfg, int64_t N);
 
 // Scratch bytes the split-K path of gemm() needs for this problem (0 if unsplit).
 size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype, bool akc = true,
@@ -90,11 +95,14 @@ hipError_t db_combine(const float* d1, int d1_splits, const float* q, int q_spli
                       hipStream_t st);
 
 // n_i = sqrt(max(0, ||W0_i||^2 + B_i . P_i)), P = sum of p_splits partials
-// [p_splits][d_out][r] (float32).  ||W0_i||^2 is the sum of the p_splits
-// partials rowsq[z][i] when rowsq is given, else it is read from W0.
-hipError_t row_norm(const void* W0, const void* B, const float* P, const float* rowsq,
-                    int p_splits, float* norm, int64_t d_out, int64_t d_in, int64_t r, int dtype,
-                    hipStream_t st);
+// [p_splits][d_out][r] (float32), ||W0_i||^2 streamed from W0.
+hipError_t row_norm(const void* W0, const void* B, const float* P, int p_splits, float* norm,
+                    int64_t d_out, int64_t d_in, int64_t r, int dtype, hipStream_t st);
+
+// n_i = sqrt(max(0, sum_z rowsq[z][i] + sum_q rowdot[q][i])), both sums in
+// index order (the partials of the projection's kEpiNorm epilogue).
+hipError_t norm_finalize(const float* rowsq, int64_t n_sq, const float* rowdot, int64_t n_dot,
+                         float* norm, int64_t d_out, hipStream_t st);
 
 // y = base + ((g-1) base + g * slora) in place on y (base), slora = s * lora.
 hipError_t compose_fwd(void* y, const void* slora, const void* m, const float* norm, int64_t T,

@@ -53,6 +53,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum of n partials p[q * stride] in index order, loads issued eight at a time.
+__device__ __forceinline__ float sum_partials(const float* p, int64_t n, int64_t stride) {
+  float acc = 0.f;
+  int64_t q = 0;
+  for (; q + 8 <= n; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(q + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; q < n; ++q) acc += p[q * stride];
+  return acc;
+}
+
 // ---- Gram finisher ------------------------------------------------------------
 // part[z], z < splits: split-K partial sums of G = A A^T, added in a fixed
 // order.  Writes (s/2) G; bf16 layers get it as a hi + lo bf16 pair
@@ -64,9 +79,7 @@ __global__ __launch_bounds__(256) void dora_gram_finalize(const float* part, int
                                                           void* g_hi, void* g_lo) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= rr) return;
-  float a = 0.f;
-  for (int z = 0; z < splits; ++z) a += part[z * rr + idx];
-  const float v = half_s * a;
+  const float v = half_s * sum_partials(part + idx, splits, rr);
   if (bf) {
     const uint16_t hi = f32_to_bf16(v);
     const float rest = v - bf16_to_f32(hi);
@@ -85,16 +98,13 @@ __global__ __launch_bounds__(256) void dora_gram_finalize(const float* part, int
 // go straight to registers) and the lane partials meet in a wave reduction.
 template <bool BF>
 __global__ __launch_bounds__(256) void dora_row_norm(const void* W0, const void* B, const float* P,
-                                                     const float* rowsq, int p_splits,
-                                                     int64_t p_stride, float* norm,
+                                                     int p_splits, int64_t p_stride, float* norm,
                                                      int64_t d_out, int64_t d_in, int64_t r) {
   using V = Vec<BF>;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= d_out) return;   // whole wave leaves; the kernel has no barrier
-  // ||W0_i||^2: from the projection's partial row sums of squares when given
-  // (then W0 is not read again), else streamed from W0.
-  const int64_t nv = rowsq ? 0 : d_in / V::kN;
+  const int64_t nv = d_in / V::kN;
   const int64_t wbase = row * nv;
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
   int64_t c = lane;
@@ -135,10 +145,20 @@ __global__ __launch_bounds__(256) void dora_row_norm(const void* W0, const void*
       acc1 = fmaf(bv[q + 3], pv[3], acc1);
     }
   }
-  if (rowsq)
-    for (int z = lane; z < p_splits; z += 64) acc2 += rowsq[(int64_t)z * d_out + row];
   const float tot = wave_sum((acc0 + acc1) + (acc2 + acc3));
   if (lane == 0) norm[row] = sqrtf(fmaxf(tot, 0.f));
+}
+
+// Row norms from the projection's per-row partials: thread = row, partial q of
+// every row contiguous, both sums in index order.
+__global__ __launch_bounds__(64) void dora_norm_finalize(const float* rowsq, int64_t n_sq,
+                                                         const float* rowdot, int64_t n_dot,
+                                                         float* norm, int64_t d_out) {
+  const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (row >= d_out) return;
+  const float base = sum_partials(rowsq + row, n_sq, d_out);
+  const float lora = sum_partials(rowdot + row, n_dot, d_out);
+  norm[row] = sqrtf(fmaxf(base + lora, 0.f));
 }
 
 // ---- compose forward ------------------------------------------------------------
@@ -263,8 +283,7 @@ __global__ __launch_bounds__(256) void dora_dm_finalize(const float* dm_part, in
   const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int64_t i = (int64_t)blockIdx.x * 64 + c;
   float s = 0.f;
-  if (i < d_out)
-    for (int64_t b = q; b < blocks; b += 4) s += dm_part[b * d_out + i];
+  if (i < d_out && q < blocks) s = sum_partials(dm_part + q * d_out + i, (blocks - q + 3) / 4, 4 * d_out);
   red[q][c] = s;
   __syncthreads();
   if (q == 0 && i < d_out)
@@ -478,18 +497,25 @@ hipError_t db_combine(const float* d1, int d1_splits, const float* q, int q_spli
   return hipGetLastError();
 }
 
-hipError_t row_norm(const void* W0, const void* B, const float* P, const float* rowsq,
-                    int p_splits, float* norm, int64_t d_out, int64_t d_in, int64_t r, int dtype,
-                    hipStream_t st) {
+hipError_t row_norm(const void* W0, const void* B, const float* P, int p_splits, float* norm,
+                    int64_t d_out, int64_t d_in, int64_t r, int dtype, hipStream_t st) {
   LaunchTimer t("row_norm", st);
   const dim3 grid((unsigned)cdiv(d_out, 4));
   const int64_t stride = d_out * r;
   if (dtype == kBF16)
-    hipLaunchKernelGGL(dora_row_norm<true>, grid, dim3(256), 0, st, W0, B, P, rowsq, p_splits,
-                       stride, norm, d_out, d_in, r);
+    hipLaunchKernelGGL(dora_row_norm<true>, grid, dim3(256), 0, st, W0, B, P, p_splits, stride,
+                       norm, d_out, d_in, r);
   else
-    hipLaunchKernelGGL(dora_row_norm<false>, grid, dim3(256), 0, st, W0, B, P, rowsq, p_splits,
-                       stride, norm, d_out, d_in, r);
+    hipLaunchKernelGGL(dora_row_norm<false>, grid, dim3(256), 0, st, W0, B, P, p_splits, stride,
+                       norm, d_out, d_in, r);
+  return hipGetLastError();
+}
+
+hipError_t norm_finalize(const float* rowsq, int64_t n_sq, const float* rowdot, int64_t n_dot,
+                         float* norm, int64_t d_out, hipStream_t st) {
+  LaunchTimer t("norm_finalize", st);
+  hipLaunchKernelGGL(dora_norm_finalize, dim3((unsigned)cdiv(d_out, 64)), dim3(64), 0, st, rowsq,
+                     n_sq, rowdot, n_dot, norm, d_out);
   return hipGetLastError();
 }
 

@@ -379,7 +379,7 @@ def test_timing_hook(ops):
         rec = ops.timing_collect()
     finally:
         ops.timing_enable(False)
-    for k in ("gram_AAt", "cross_gram_proj", "row_norm", "fused_fwd_gemm", "compose_bwd", "dx_gemm"):
+    for k in ("gram_AAt", "cross_gram_proj", "norm_finalize", "fused_fwd_gemm", "compose_bwd", "dx_gemm"):
         assert k in rec and rec[k][0] >= 1 and rec[k][1] > 0, (k, rec)
     assert ops.timing_collect() == {}
 
