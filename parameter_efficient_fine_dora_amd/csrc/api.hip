@@ -101,6 +101,7 @@ struct Layout {
          hlo = 0, d1 = 0;
   int qsplits = 1, hsplits = 1, d1splits = 1;
   size_t scratch = 0, scratch_bytes = 0;         // split-K partial sums
+  size_t scratch2 = 0, scratch2_bytes = 0;       // backward: dB's partials on the side stream
   size_t total = 0;
   int splits = 1, psplits = 1;
   int64_t dm_blocks = 0;
@@ -160,6 +161,8 @@ Layout layout(const dora_shape& s, int op) {
     need(s.tokens, s.d_in, s.d_out + s.r, true, false);  // dx
     need(s.d_out, s.r, s.tokens, false, false);          // dB
     need(s.r, s.d_in, s.tokens, false, false);           // dA
+    L.scratch2_bytes = gemm_scratch_bytes(s.d_out, s.r, s.tokens, dt, false, false);
+    L.scratch2 = take(L.scratch2_bytes);
     if ((s.flags & DORA_FLAG_EXACT_NORM_GRAD) && s.r > 0) {
       L.dm = take((size_t)s.d_out * 4);
       L.kappa = take((size_t)s.d_out * 4);
@@ -183,6 +186,53 @@ Layout layout(const dora_shape& s, int op) {
   L.scratch_bytes = scratch;
   L.total = off;
   return L;
+}
+
+// A second stream for work that does not depend on the caller's stream's
+// current chain (e.g. the down-projection beside the norm).  One per host
+// thread and device, default priority, created on first use and kept for the
+// life of the process; fork and join go through events, so the pair works
+// under stream capture too.  Returns null (run everything on the caller's
+// stream) if it cannot be created, and while the timing hook is on, so that
+// each kernel's events bracket that kernel alone.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+SideStream* side_stream() {
+  if (g_timing.load(std::memory_order_relaxed)) return nullptr;
+  constexpr int kMaxDevices = 64;
+  static thread_local SideStream per_dev[kMaxDevices];
+  static thread_local bool failed[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices || failed[dev])
+    return nullptr;
+  SideStream& ss = per_dev[dev];
+  if (!ss.s) {
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      failed[dev] = true;
+      ss.s = nullptr;
+      return nullptr;
+    }
+  }
+  return &ss;
+}
+
+// Side stream `side` starts after everything enqueued on `st` so far.
+hipError_t fork_to(hipStream_t st, SideStream* side) {
+  hipError_t e = hipEventRecord(side->fork, st);
+  if (e != hipSuccess) return e;
+  return hipStreamWaitEvent(side->s, side->fork, 0);
+}
+
+// Work enqueued on `st` from now on waits for everything enqueued on `side`.
+hipError_t join_from(SideStream* side, hipStream_t st) {
+  hipError_t e = hipEventRecord(side->join, side->s);
+  if (e != hipSuccess) return e;
+  return hipStreamWaitEvent(st, side->join, 0);
 }
 
 // Validation-only op id of calls that take no workspace.
@@ -227,6 +277,12 @@ uint8_t* at(void* ws, size_t off) { return reinterpret_cast<uint8_t*>(ws) + off;
 void give_scratch(GemmProblem& g, void* ws, const Layout& L) {
   g.scratch = L.scratch_bytes ? at(ws, L.scratch) : nullptr;
   g.scratch_bytes = L.scratch_bytes;
+}
+
+// The backward's second split-K region, for dB while ts runs beside it.
+void give_scratch2(GemmProblem& g, void* ws, const Layout& L) {
+  g.scratch = L.scratch2_bytes ? at(ws, L.scratch2) : nullptr;
+  g.scratch_bytes = L.scratch2_bytes;
 }
 
 // Factored norm: G = A A^T (split-K), (s/2) G -> hi/lo, P = 2s W0 A^T + s^2 B G,
@@ -354,12 +410,12 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   const int dt = s.dtype;
 
-  DORA_CHECK(run_norm(s, W0, A, B, norm_out, ws, L, st));
-  if (noT) return DORA_OK;
-
-  // xs = s (x A^T): the down-projection, pre-scaled by s.
+  // xs = s (x A^T): the down-projection, pre-scaled by s.  It does not depend
+  // on the norm (and uses other workspace regions), so it runs on a side
+  // stream beside the norm's chain and joins before the forward GEMM.
   void* xs = xs_out ? xs_out : at(ws, L.xs);
-  if (s.r > 0) {
+  SideStream* side = (!noT && s.r > 0) ? side_stream() : nullptr;
+  auto down_proj = [&](hipStream_t on) -> int {
     GemmProblem d;
     d.M = s.tokens;
     d.N = s.r;
@@ -369,8 +425,18 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
     d.c = xs;
     d.ldc = s.r;
     give_scratch(d, ws, L);
-    HIP_TRY(gemm(d, dt, st, "down_proj_xs"));
+    HIP_TRY(gemm(d, dt, on, "down_proj_xs"));
+    return DORA_OK;
+  };
+  if (side) {
+    HIP_TRY(fork_to(st, side));
+    DORA_CHECK(down_proj(side->s));
   }
+  const int rc_norm = run_norm(s, W0, A, B, norm_out, ws, L, st);
+  if (side) HIP_TRY(join_from(side, st));   // joined even if the norm failed
+  DORA_CHECK(rc_norm);
+  if (noT) return DORA_OK;
+  if (!side && s.r > 0) DORA_CHECK(down_proj(st));
 
   if (s.flags & DORA_FLAG_SEPARATE_COMPOSE) {
     // base = x W0^T into y; slora = xs B^T; then the one-pass compose.
@@ -446,16 +512,53 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
   void* gz = at(ws, L.gz);
   float* dmpart = reinterpret_cast<float*>(at(ws, L.dmpart));
   const bool need_gz = (grad_x && !noT) || (has_r && (grad_A || grad_B));
+  float* kappa = nullptr;   // A.1: k' and Q (set below when the norm is undetached)
+  float* q = nullptr;
   float* dm = grad_m ? grad_m : (exact ? reinterpret_cast<float*>(at(ws, L.dm)) : nullptr);
   if (need_gz || dm)
     HIP_TRY(compose_bwd(grad_y, y, m, norm, gz, dmpart, s.tokens, s.d_out, kTokPerDmBlock, dt, st));
-  if (dm) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, dt, st));
+  // With the norm detached, dm and dB = gz^T xs depend only on compose_bwd's
+  // outputs (and the saved xs): they run on a side stream (dB with its own
+  // split-K region) beside ts, and join before the call returns.
+  SideStream* side = (!exact && has_r && grad_B && xs && !noT) ? side_stream() : nullptr;
+  auto grad_b = [&](hipStream_t on, bool second_scratch, const void* xsu) -> int {
+    GemmProblem b;
+    b.M = s.d_out;
+    b.N = s.r;
+    b.nseg = 1;
+    b.seg[0] = {gz, xsu, s.d_out, s.r, s.tokens};
+    b.a_kcontig = false;
+    b.b_kcontig = false;
+    b.c = grad_B;
+    b.ldc = s.r;
+    if (second_scratch)
+      give_scratch2(b, ws, L);
+    else
+      give_scratch(b, ws, L);
+    if (exact) {   // float32 partial sums, combined with diag(k') Q in one rounding
+      float* d1 = reinterpret_cast<float*>(at(ws, L.d1));
+      b.c = d1;
+      b.out_f32 = true;
+      b.split = L.d1splits;
+      b.split_stride = s.d_out * s.r;
+      HIP_TRY(gemm(b, dt, on, "dB_gemm"));
+      HIP_TRY(db_combine(d1, L.d1splits, q, L.qsplits, kappa, grad_B, s.d_out, s.r, dt, on));
+    } else {
+      HIP_TRY(gemm(b, dt, on, "dB_gemm"));
+    }
+    return DORA_OK;
+  };
+  if (side) {
+    HIP_TRY(fork_to(st, side));
+    if (dm) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, dt, side->s));
+    DORA_CHECK(grad_b(side->s, true, xs));
+  } else if (dm) {
+    HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, dt, st));
+  }
 
   // A.1 terms: k' = -s m dm / n^2, Bk' = diag(k') B, Q = W0 A^T + s B G,
   // H' = s Bk'^T B.  Then dB += diag(k') Q and dA += Bk'^T W0 + H' A.
-  float* kappa = nullptr;
   void* bk = nullptr;
-  float* q = nullptr;
   void* hmat = nullptr;
   if (exact) {
     kappa = reinterpret_cast<float*>(at(ws, L.kappa));
@@ -543,7 +646,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     HIP_TRY(gemm(d, dt, st, "dx_gemm"));
   }
 
-  if (grad_B && has_r) {
+  if (grad_B && has_r && !side) {
     const void* xsu = xs;
     if (!xsu && !noT) {
       void* xw = at(ws, L.xs);
@@ -559,27 +662,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
       HIP_TRY(gemm(d, dt, st, "down_proj_xs"));
       xsu = xw;
     }
-    GemmProblem b;
-    b.M = s.d_out;
-    b.N = s.r;
-    b.nseg = 1;
-    b.seg[0] = {gz, xsu, s.d_out, s.r, s.tokens};
-    b.a_kcontig = false;
-    b.b_kcontig = false;
-    b.c = grad_B;
-    b.ldc = s.r;
-    give_scratch(b, ws, L);
-    if (exact) {   // float32 partial sums, combined with diag(k') Q in one rounding
-      float* d1 = reinterpret_cast<float*>(at(ws, L.d1));
-      b.c = d1;
-      b.out_f32 = true;
-      b.split = L.d1splits;
-      b.split_stride = s.d_out * s.r;
-      HIP_TRY(gemm(b, dt, st, "dB_gemm"));
-      HIP_TRY(db_combine(d1, L.d1splits, q, L.qsplits, kappa, grad_B, s.d_out, s.r, dt, st));
-    } else {
-      HIP_TRY(gemm(b, dt, st, "dB_gemm"));
-    }
+    DORA_CHECK(grad_b(st, false, xsu));
   }
 
   if (grad_A && has_r) {
@@ -600,6 +683,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     give_scratch(a, ws, L);
     HIP_TRY(gemm(a, dt, st, "dA_gemm"));
   }
+  if (side) HIP_TRY(join_from(side, st));
   return DORA_OK;
 }
 

@@ -384,6 +384,25 @@ def test_timing_hook(ops):
     assert ops.timing_collect() == {}
 
 
+def test_side_stream_overlap_matches_serial(ops):
+    """The down-projection (forward) and dm, dB (backward) run on a side stream
+    beside the norm and ts; with the timing hook on, everything runs on the
+    caller's stream.  Both orders must give the same bits (no shared buffer)."""
+    shape = LayerShape(520, 1032, 136, 300, 2.0, "bf16")
+    layer = synth.make_layer(shape, 17, grad=True)
+    outs = []
+    for timing in (False, True, False):
+        ops.timing_enable(timing)
+        try:
+            outs.append(run_layer(ops, shape, layer))
+        finally:
+            ops.timing_enable(False)
+            ops.timing_collect()
+    for k in outs[0]:
+        for o in outs[1:]:
+            assert np.array_equal(outs[0][k], o[k]), k
+
+
 def test_bad_arguments_raise_before_launch(ops):
     from parameter_efficient_fine_dora_amd._lib import DoraError, ERR_CODE
     W0 = torch.zeros(16, 17, dtype=torch.bfloat16, device="cuda")[:, 1:]
