@@ -205,6 +205,28 @@ DORA_API const char* dora_strerror(int code);
 DORA_API int dora_timing_enable(int enable);
 DORA_API int dora_timing_collect(char* buf, size_t buflen);
 
+/*
+ * Measurement probe: the sustained dense bf16 MFMA rate.  Launches `blocks`
+ * workgroups of four waves on hip_stream; each wave runs four independent
+ * chains of `iters` v_mfma_f32_32x32x16_bf16 on register operands and writes
+ * one checksum per thread to out (device, blocks * 256 floats, caller-owned).
+ * Time it with events on the same stream; dora_probe_mfma_flops gives the
+ * flops one such launch performs.  Returns DORA_ERR_SHAPE for iters < 1,
+ * blocks < 1 or a NULL out, DORA_ERR_HIP if the launch fails.
+ */
+DORA_API int dora_probe_mfma(int64_t iters, int blocks, float* out, void* hip_stream);
+DORA_API double dora_probe_mfma_flops(int64_t iters, int blocks);
+
+/*
+ * Measurement probe: the streaming HBM rate.  c = a + b elementwise over
+ * `bytes` bytes of float32 (two streams read, one written: 3 * bytes of
+ * traffic), device pointers, caller-owned, 16-byte aligned, c not aliasing a
+ * or b.  Returns DORA_ERR_NULL, DORA_ERR_SHAPE (bytes not a positive multiple
+ * of 16), DORA_ERR_ALIGN or DORA_ERR_HIP.
+ */
+DORA_API int dora_probe_stream(const void* a, const void* b, void* c, int64_t bytes,
+                               void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,9 @@ _SIGS = {
     "dora_strerror": (ctypes.c_char_p, [_i]),
     "dora_timing_enable": (_i, [_i]),
     "dora_timing_collect": (_i, [ctypes.c_char_p, _sz]),
+    "dora_probe_mfma": (_i, [ctypes.c_int64, _i, _vp, _vp]),
+    "dora_probe_mfma_flops": (ctypes.c_double, [ctypes.c_int64, _i]),
+    "dora_probe_stream": (_i, [_vp, _vp, _vp, ctypes.c_int64, _vp]),
 }
 
 

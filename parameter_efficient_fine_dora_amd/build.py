@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdora.so")
-SOURCES = ["api.hip", "gemm.hip", "rowwise.hip"]
+SOURCES = ["api.hip", "gemm.hip", "rowwise.hip", "probe.hip"]
 HEADERS = ["common.h", "kernels.h"]
 ARCH = "gfx950"
 

@@ -639,7 +639,8 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
 // float32 layers: 64x64 tiles, 16-deep K steps, 4x4 outputs per thread.
 template <bool AKC, bool BKC, int EPI>
 __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
-  constexpr int BM = 64, BN = 64, BKF = 16;
+  constexpr int BM = 64, BN = 64, BKF = kBK;   // one 64-deep step per round
+  constexpr int kPer = BM * BKF / 256;          // elements of each operand per thread and round
   __shared__ float As[BKF][BM + 4];
   __shared__ float Bs[BKF][BN + 4];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -651,44 +652,50 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
   const int kt_hi = min(kt_lo + p.kt_per_split, kt_total);
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
     const int s = kt < p.kt_end[0] ? 0 : (kt < p.kt_end[1] ? 1 : 2);
-    const int kbase = (kt - (s == 0 ? 0 : (s == 1 ? p.kt_end[0] : p.kt_end[1]))) * kBK;
+    const int k0 = (kt - (s == 0 ? 0 : (s == 1 ? p.kt_end[0] : p.kt_end[1]))) * kBK;
     const float* a = reinterpret_cast<const float*>(s == 0 ? p.a[0] : (s == 1 ? p.a[1] : p.a[2]));
     const float* b = reinterpret_cast<const float*>(s == 0 ? p.b[0] : (s == 1 ? p.b[1] : p.b[2]));
     const int64_t lda = s == 0 ? p.lda[0] : (s == 1 ? p.lda[1] : p.lda[2]);
     const int64_t ldb = s == 0 ? p.ldb[0] : (s == 1 ? p.ldb[1] : p.ldb[2]);
     const int Ks = s == 0 ? p.K[0] : (s == 1 ? p.K[1] : p.K[2]);
-    for (int ks = 0; ks < kBK; ks += BKF) {
-      const int k0 = kbase + ks;
-      if (k0 >= Ks) break;
-      for (int e = tid; e < BM * BKF; e += 256) {
-        const int mm = AKC ? e / BKF : e % BM, kk = AKC ? e % BKF : e / BM;
-        const int gm = m0 + mm, gk = k0 + kk;
-        float va = 0.f;
-        if (gm < p.M && gk < Ks)
-          va = AKC ? a[(int64_t)gm * lda + gk] : a[(int64_t)gk * lda + gm];
-        As[kk][mm] = va;
-        const int nn = BKC ? e / BKF : e % BN, kb = BKC ? e % BKF : e / BN;
-        const int gn = n0 + nn, gk2 = k0 + kb;
-        float vb = 0.f;
-        if (gn < p.N && gk2 < Ks)
-          vb = BKC ? b[(int64_t)gn * ldb + gk2] : b[(int64_t)gk2 * ldb + gn];
-        Bs[kb][nn] = vb;
-      }
-      __syncthreads();
+    // Every load of the round is issued before the first LDS store, so a
+    // round costs one memory latency.  Element e of a K-contiguous operand is
+    // (row e / 64, k e % 64): 64 lanes read one row's 256 contiguous bytes.
+    float va[kPer], vb[kPer];
 #pragma unroll
-      for (int kk = 0; kk < BKF; ++kk) {
-        float ra[4], rb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = As[kk][ty * 4 + i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) rb[j] = Bs[kk][tx * 4 + j];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ra[i], rb[j], acc[i][j]);
-      }
-      __syncthreads();
+    for (int i = 0; i < kPer; ++i) {
+      const int e = tid + i * 256;
+      const int mm = AKC ? e / BKF : e % BM, kk = AKC ? e % BKF : e / BM;
+      const int gm = m0 + mm, gk = k0 + kk;
+      va[i] = (gm < p.M && gk < Ks) ? (AKC ? a[(int64_t)gm * lda + gk] : a[(int64_t)gk * lda + gm])
+                                    : 0.f;
+      const int nn = BKC ? e / BKF : e % BN, kb = BKC ? e % BKF : e / BN;
+      const int gn = n0 + nn, gk2 = k0 + kb;
+      vb[i] = (gn < p.N && gk2 < Ks) ? (BKC ? b[(int64_t)gn * ldb + gk2] : b[(int64_t)gk2 * ldb + gn])
+                                     : 0.f;
     }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = tid + i * 256;
+      const int mm = AKC ? e / BKF : e % BM, kk = AKC ? e % BKF : e / BM;
+      As[kk][mm] = va[i];
+      const int nn = BKC ? e / BKF : e % BN, kb = BKC ? e % BKF : e / BN;
+      Bs[kb][nn] = vb[i];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < BKF; ++kk) {
+      float ra[4], rb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ra[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rb[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ra[i], rb[j], acc[i][j]);
+    }
+    __syncthreads();
   }
   float* c = reinterpret_cast<float*>(p.c) + blockIdx.y * p.split_stride;
   const int n = n0 + tx * 4;
@@ -716,10 +723,12 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
 }
 
 // ---- split-K reduction ----------------------------------------------------------
-// out[i] = alpha * sum_{z < S} part[z][i] over M*N elements, fixed order.
+// out[i] = alpha * sum_{z < S} part[z][i] over M*N elements, fixed order; with
+// mag given (float32 layers), the compose epilogue is applied to the sum.
 __global__ __launch_bounds__(256) void dora_splitk_reduce(const float* part, int S, int64_t n4,
                                                           int64_t stride, float alpha, void* out,
-                                                          int out_bf16) {
+                                                          int out_bf16, const float* mag,
+                                                          const float* nrm, int N) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   // partials added in index order, their loads issued four at a time
@@ -734,6 +743,10 @@ __global__ __launch_bounds__(256) void dora_splitk_reduce(const float* part, int
       if (z0 + u < S) acc = (z0 + u == 0) ? v[u] : acc + v[u];
   }
   acc *= alpha;
+  if (mag) {   // compose epilogue of a float32 layer: y = z + (g - 1) z per column
+    const f32x4 gm1 = gm1_4<false>(mag, nrm, (int)((i * 4) % N));
+    acc += gm1 * acc;
+  }
   if (out_bf16)
     reinterpret_cast<u32x2*>(out)[i] = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
   else
@@ -885,14 +898,21 @@ hipError_t run(int cfg, int split, const GemmProblem& p, KArgs& a, int kt, hipSt
 }  // namespace
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bkc) {
-  if (dtype == kF32 || M <= 0 || N <= 0) return {-1, 1};
+  if (M <= 0 || N <= 0) return {-1, 1};
   const int64_t ktiles = cdiv64(K, kBK);
+  if (dtype == kF32) {
+    // 64 x 64 VALU tiles (one wave per SIMD, latency-bound per workgroup): split K,
+    // down to one 64-deep step per split, up to ~256 workgroups
+    const int64_t t = cdiv64(M, 64) * cdiv64(N, 64);
+    int64_t split = std::min<int64_t>((256 + t - 1) / t, std::max<int64_t>(1, ktiles));
+    return {-1, (int)std::max<int64_t>(1, std::min<int64_t>(split, 16))};
+  }
   auto tiles = [&](int cfg) { return cdiv64(M, kCfgs[cfg].bm) * cdiv64(N, kCfgs[cfg].bn); };
   const bool both_mc = !akc && !bkc;
   // Large outputs: 256 x 256 tiles (8 waves), then 256 x 128 (8 waves).  Two
   // transposed operands take the 256 x 128 tile (register budget).
   if (!both_mc && tiles(0) >= 256) return {0, 1};
-  if (tiles(5) >= 200) return {5, 1};
+  if (tiles(5) >= 256) return {5, 1};   // only when it still fills every CU
   // Skinny or small, split along K: 128 x 128 tiles at ~384 workgroups did best
   // for every operand layout of the d = 8192, r = 384 layer (xs, P, ts, dB, dA).
   const int cfg = 2;
@@ -926,16 +946,45 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
        !p.add || p.N % 4 != 0 || p.nseg < 1 || p.seg[0].K <= 0))
     return hipErrorInvalidValue;
   if (dtype == kF32) {
-    LaunchTimer timer(label, st);
     a.tiles_m = (int)cdiv64(p.M, 64);
     a.tiles_n = (int)cdiv64(p.N, 64);
-    const int split = p.split < 1 ? 1 : p.split;
-    a.kt_per_split = split > 1 ? (kt + split - 1) / split : (kt > 0 ? kt : 1);
-    const dim3 grid(a.tiles_m * a.tiles_n, split);
-    if (p.a_kcontig && p.b_kcontig) return launch_f32<true, true>(a, p.epi, grid, st);
-    if (p.a_kcontig) return launch_f32<true, false>(a, p.epi, grid, st);
-    if (p.b_kcontig) return launch_f32<false, true>(a, p.epi, grid, st);
-    return launch_f32<false, false>(a, p.epi, grid, st);
+    auto launch = [&](KArgs& args, int split, int epi) {
+      args.kt_per_split = split > 1 ? (kt + split - 1) / split : (kt > 0 ? kt : 1);
+      const dim3 grid(args.tiles_m * args.tiles_n, split);
+      if (p.a_kcontig && p.b_kcontig) return launch_f32<true, true>(args, epi, grid, st);
+      if (p.a_kcontig) return launch_f32<true, false>(args, epi, grid, st);
+      if (p.b_kcontig) return launch_f32<false, true>(args, epi, grid, st);
+      return launch_f32<false, false>(args, epi, grid, st);
+    };
+    if (p.split > 1 || p.out_f32) {   // caller-managed partial sums
+      LaunchTimer timer(label, st);
+      return launch(a, p.split < 1 ? 1 : p.split, p.epi);
+    }
+    const int split = p.force_split > 0 ? p.force_split : plan_gemm(p.M, p.N, K, dtype).split;
+    const size_t need = (size_t)split * p.M * p.N * 4;
+    if (split > 1 && (p.epi == kEpiStore || p.epi == kEpiCompose) && p.scratch &&
+        p.scratch_bytes >= need && p.ldc == p.N) {
+      KArgs b = a;   // float32 partials into scratch, then the fixed-order reduction
+      b.c = p.scratch;
+      b.ldc = p.N;
+      b.split_stride = p.M * p.N;
+      b.alpha = 1.f;
+      {
+        LaunchTimer timer(label, st);
+        const hipError_t e = launch(b, split, kEpiStore);   // plain partials; the epilogue follows
+        if (e != hipSuccess) return e;
+      }
+      LaunchTimer timer("splitk_reduce", st);
+      const int64_t n4 = p.M * p.N / 4;
+      const bool compose = p.epi == kEpiCompose;
+      hipLaunchKernelGGL(dora_splitk_reduce, dim3((unsigned)cdiv64(n4, 256)), dim3(256), 0, st,
+                         reinterpret_cast<const float*>(p.scratch), split, n4, p.M * p.N, p.alpha,
+                         p.c, 0, compose ? reinterpret_cast<const float*>(p.mag) : nullptr,
+                         compose ? p.norm : nullptr, (int)p.N);
+      return hipGetLastError();
+    }
+    LaunchTimer timer(label, st);
+    return launch(a, 1, p.epi);
   }
 
   int cfg = p.cfg;
@@ -965,7 +1014,7 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
     const int64_t n4 = p.M * p.N / 4;
     hipLaunchKernelGGL(dora_splitk_reduce, dim3((unsigned)cdiv64(n4, 256)), dim3(256), 0, st,
                        reinterpret_cast<const float*>(p.scratch), pl.split, n4, p.M * p.N, p.alpha,
-                       p.c, 1);
+                       p.c, 1, nullptr, nullptr, (int)p.N);
     return hipGetLastError();
   }
   LaunchTimer timer(label, st);

@@ -230,3 +230,30 @@ def timing_collect() -> dict:
     if rc < 0:
         raise DoraError(rc, "dora_timing_collect")
     return {k: (int(v[0]), float(v[1])) for k, v in json.loads(buf.value.decode()).items()}
+
+
+def probe_mfma(iters: int, blocks: int, *, out=None):
+    """Launch the sustained-MFMA probe on the current stream; returns (out, flops)."""
+    import torch
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    L = _lib.lib()
+    rc = L.dora_probe_mfma(int(iters), int(blocks), out.data_ptr(), st)
+    if rc != 0:
+        raise DoraError(rc, "dora_probe_mfma")
+    return out, L.dora_probe_mfma_flops(int(iters), int(blocks))
+
+
+def probe_stream(a, b, c):
+    """c = a + b over float32 tensors on the current stream (HBM streaming probe)."""
+    import torch
+    for t in (a, b, c):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != a.numel():
+            raise ValueError("probe_stream takes three contiguous float32 tensors of one size")
+    st = torch.cuda.current_stream().cuda_stream
+    rc = _lib.lib().dora_probe_stream(a.data_ptr(), b.data_ptr(), c.data_ptr(), a.numel() * 4, st)
+    if rc != 0:
+        raise DoraError(rc, "dora_probe_stream")
+    return c
+

@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
     names = set(declared_symbols())
     assert {"dora_norm", "dora_forward", "dora_backward", "dora_merge", "dora_vera_scale",
             "dora_vera_grads", "dora_workspace_bytes",
-            "dora_strerror", "dora_timing_enable", "dora_timing_collect"} <= names
+            "dora_strerror", "dora_timing_enable", "dora_timing_collect", "dora_probe_mfma",
+            "dora_probe_mfma_flops", "dora_probe_stream"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -176,3 +177,21 @@ def test_library_has_no_device_allocation_calls():
         text = open(os.path.join(csrc, fn)).read()
         for bad in ("hipMalloc", "hipFree", "hipHostMalloc", "hipExtMalloc"):
             assert bad not in text, (fn, bad)
+
+
+def test_mfma_probe_validation_and_flop_count():
+    L = _lib.lib()
+    shape_err = [k for k, v in _lib.ERR.items() if v == "DORA_ERR_SHAPE"][0]
+    assert L.dora_probe_mfma(0, 1, None, None) == shape_err        # no launch
+    assert L.dora_probe_mfma(1, 0, None, None) == shape_err
+    # blocks * 4 waves * iters * 4 chains * (2 * 32 * 32 * 16) flops
+    assert L.dora_probe_mfma_flops(10, 3) == 3 * 4 * 10 * 4 * 32768
+
+
+def test_stream_probe_validation():
+    L = _lib.lib()
+    E = _lib.ERR_CODE
+    assert L.dora_probe_stream(None, None, None, 16, None) == E["DORA_ERR_NULL"]
+    assert L.dora_probe_stream(16, 32, 48, 8, None) == E["DORA_ERR_SHAPE"]      # not a multiple of 16
+    assert L.dora_probe_stream(16, 32, 52, 16, None) == E["DORA_ERR_ALIGN"]     # c misaligned
+

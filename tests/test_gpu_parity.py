@@ -403,6 +403,23 @@ def test_side_stream_overlap_matches_serial(ops):
             assert np.array_equal(outs[0][k], o[k]), k
 
 
+def test_measurement_probes(ops):
+    """The bench's peak probes: the stream probe computes c = a + b exactly; the
+    MFMA probe's checksum is finite and the same on every launch."""
+    g = torch.Generator(device="cuda").manual_seed(5)
+    n = (1 << 20) + 12   # a grid-stride tail
+    a = torch.randn(n, device="cuda", generator=g)
+    b = torch.randn(n, device="cuda", generator=g)
+    c = torch.empty_like(a)
+    ops.probe_stream(a, b, c)
+    assert torch.equal(c, a + b)
+    out1, flops = ops.probe_mfma(64, 8)
+    first = out1.clone()
+    ops.probe_mfma(64, 8, out=out1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(first).all() and torch.equal(first, out1) and flops == 8 * 4 * 64 * 4 * 32768
+
+
 def test_bad_arguments_raise_before_launch(ops):
     from parameter_efficient_fine_dora_amd._lib import DoraError, ERR_CODE
     W0 = torch.zeros(16, 17, dtype=torch.bfloat16, device="cuda")[:, 1:]
