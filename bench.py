@@ -212,6 +212,9 @@ def main():
                          "time each step alone")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the achievable HBM and MFMA rates")
+    ap.add_argument("--serial", action="store_true",
+                    help="keep every kernel on one stream (the library's timing hook on for "
+                         "all steps), so that profiles see one launch order")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the DoRA layer's "
@@ -276,10 +279,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.serial:
+        ops.timing_enable(True)
     print("# warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.serial:
+        ops.timing_collect()   # drop the warm-up records
 
     print(f"# timing {args.steps} steps{' (cold)' if args.cold else ''}", file=sys.stderr,
           flush=True)
@@ -316,6 +323,8 @@ def main():
     torch.cuda.synchronize()
     ops.timing_enable(False)
     timing = ops.timing_collect()
+    if args.serial:   # the timed steps' records, then the per-kernel pass's (same kernels)
+        timing = {k: (v[0] / 2, v[1] / 2) for k, v in timing.items()}
 
     peaks = None
     if not args.no_peaks:
@@ -326,7 +335,8 @@ def main():
     headline = args.config == DEFAULT_CONFIG and not flags and not args.cold
     traffic = recorded_traffic() if headline else {}
     kernels = kernel_table(timing, args.steps, work, traffic, peaks, flop_peak)
-    dominant = max(timing, key=lambda k: timing[k][1])
+    # the dominant kernel among those with a work model (split-K reductions have none)
+    dominant = max((k for k in timing if k in work), key=lambda k: timing[k][1])
     kind, amount = work[dominant]
     avg_s = timing[dominant][1] / timing[dominant][0] * 1e-3
     if kind == "flop":
