@@ -9,7 +9,7 @@ before the timed region; every output and workspace buffer is allocated
 before it too.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--config NAME] [--cold] [--separate-compose] [--no-peaks]
+                    [--config NAME] [--cold] [--graph] [--separate-compose] [--no-peaks]
 
 Prints one JSON line.  ``value`` is microseconds per step (lower is better).
 ``roofline`` covers the dominant kernel (largest share of the step), timed
@@ -212,6 +212,8 @@ def main():
                          "time each step alone")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the achievable HBM and MFMA rates")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step as a HIP graph and time its replays")
     ap.add_argument("--serial", action="store_true",
                     help="keep every kernel on one stream (the library's timing hook on for "
                          "all steps), so that profiles see one launch order")
@@ -288,8 +290,26 @@ def main():
     if args.serial:
         ops.timing_collect()   # drop the warm-up records
 
-    print(f"# timing {args.steps} steps{' (cold)' if args.cold else ''}", file=sys.stderr,
-          flush=True)
+    run = step
+    if args.graph:
+        # capture one step (the library's side stream joins the capture through
+        # its fork/join events); every buffer is already allocated
+        print("# capturing one step as a graph", file=sys.stderr, flush=True)
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step()
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        run = graph.replay
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+    print(f"# timing {args.steps} steps{' (cold)' if args.cold else ''}"
+          f"{' (graph replays)' if args.graph else ''}", file=sys.stderr, flush=True)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -299,7 +319,7 @@ def main():
         for _ in range(args.steps):
             evict.fill_(1)
             ev0.record()
-            step()
+            run()
             ev1.record()
             torch.cuda.synchronize()
             per.append(ev0.elapsed_time(ev1))
@@ -307,7 +327,7 @@ def main():
     else:
         ev0.record()
         for _ in range(args.steps):
-            step()
+            run()
         ev1.record()
         torch.cuda.synchronize()
         ms_per_step = ev0.elapsed_time(ev1) / args.steps
@@ -376,6 +396,7 @@ def main():
                    "d_out": d_out, "d_in": d_in, "r": r, "tokens": T, "s": s,
                    "compose": "separate" if flags else "gemm-fused",
                    "cache": "cold (MALL evicted before each step)" if args.cold else "warm",
+                   "launch": "HIP graph replay" if args.graph else "eager",
                    "parallelism": "dp1"},
         "roofline": roof,
         "cpu_baseline": cpu,
