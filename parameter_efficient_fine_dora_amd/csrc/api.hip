@@ -143,9 +143,9 @@ Layout layout(const dora_shape& s, int op) {
   }
   if (op == DORA_OP_FORWARD) {
     L.xs = take(T * r * e);
-    // float32 layers split the fused GEMM's K too (its compose runs in the reduction)
-    if (s.dtype == kF32 && !(s.flags & DORA_FLAG_SEPARATE_COMPOSE))
-      need(s.tokens, s.d_out, s.d_in + s.r);
+    // the fused GEMM splits K when its tiles cannot fill the chip (the compose
+    // then runs in the fixed-order reduction)
+    if (!(s.flags & DORA_FLAG_SEPARATE_COMPOSE)) need(s.tokens, s.d_out, s.d_in + s.r);
     if (s.flags & DORA_FLAG_SEPARATE_COMPOSE) {
       L.slora = take(T * (size_t)s.d_out * e);
       need(s.tokens, s.d_out, s.d_in);

@@ -724,11 +724,11 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
 
 // ---- split-K reduction ----------------------------------------------------------
 // out[i] = alpha * sum_{z < S} part[z][i] over M*N elements, fixed order; with
-// mag given (float32 layers), the compose epilogue is applied to the sum.
+// mag given, the compose epilogue is applied to the sum.
 __global__ __launch_bounds__(256) void dora_splitk_reduce(const float* part, int S, int64_t n4,
                                                           int64_t stride, float alpha, void* out,
-                                                          int out_bf16, const float* mag,
-                                                          const float* nrm, int N) {
+                                                          int out_bf16, const void* mag,
+                                                          int mag_bf16, const float* nrm, int N) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   // partials added in index order, their loads issued four at a time
@@ -743,8 +743,9 @@ __global__ __launch_bounds__(256) void dora_splitk_reduce(const float* part, int
       if (z0 + u < S) acc = (z0 + u == 0) ? v[u] : acc + v[u];
   }
   acc *= alpha;
-  if (mag) {   // compose epilogue of a float32 layer: y = z + (g - 1) z per column
-    const f32x4 gm1 = gm1_4<false>(mag, nrm, (int)((i * 4) % N));
+  if (mag) {   // compose epilogue: y = z + (g - 1) z per column, as the GEMM epilogue forms it
+    const int n = (int)((i * 4) % N);
+    const f32x4 gm1 = mag_bf16 ? gm1_4<true>(mag, nrm, n) : gm1_4<false>(mag, nrm, n);
     acc += gm1 * acc;
   }
   if (out_bf16)
@@ -979,8 +980,8 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
       const bool compose = p.epi == kEpiCompose;
       hipLaunchKernelGGL(dora_splitk_reduce, dim3((unsigned)cdiv64(n4, 256)), dim3(256), 0, st,
                          reinterpret_cast<const float*>(p.scratch), split, n4, p.M * p.N, p.alpha,
-                         p.c, 0, compose ? reinterpret_cast<const float*>(p.mag) : nullptr,
-                         compose ? p.norm : nullptr, (int)p.N);
+                         p.c, 0, compose ? p.mag : nullptr, 0, compose ? p.norm : nullptr,
+                         (int)p.N);
       return hipGetLastError();
     }
     LaunchTimer timer(label, st);
@@ -997,8 +998,12 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
   if (p.cfg >= 0) pl.cfg = cfg;
   if (p.force_split > 0) pl.split = p.force_split;
   const size_t need = (size_t)pl.split * p.M * p.N * 4;
-  if (pl.split > 1 && p.epi == kEpiStore && p.scratch && p.scratch_bytes >= need) {
-    // Split-K: float32 partials into scratch, then a fixed-order reduction.
+  if (pl.split > 1 && (p.epi == kEpiStore || p.epi == kEpiCompose) && p.scratch &&
+      p.scratch_bytes >= need && p.ldc == p.N) {
+    // Split-K: float32 partials into scratch, then a fixed-order reduction
+    // (which applies the compose epilogue when there is one).
+    GemmProblem q = p;
+    q.epi = kEpiStore;
     KArgs b = a;
     b.c = p.scratch;
     b.ldc = p.N;
@@ -1006,15 +1011,16 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
     b.alpha = 1.f;
     {
       LaunchTimer timer(label, st);
-      const hipError_t e = run(pl.cfg, pl.split, p, b, kt, st, true);
+      const hipError_t e = run(pl.cfg, pl.split, q, b, kt, st, true);
       if (e != hipSuccess) return e;
     }
-    if (p.ldc != p.N) return hipErrorInvalidValue;
+    const bool compose = p.epi == kEpiCompose;
     LaunchTimer timer("splitk_reduce", st);
     const int64_t n4 = p.M * p.N / 4;
     hipLaunchKernelGGL(dora_splitk_reduce, dim3((unsigned)cdiv64(n4, 256)), dim3(256), 0, st,
                        reinterpret_cast<const float*>(p.scratch), pl.split, n4, p.M * p.N, p.alpha,
-                       p.c, 1, nullptr, nullptr, (int)p.N);
+                       p.c, 1, compose ? p.mag : nullptr, 1, compose ? p.norm : nullptr,
+                       (int)p.N);
     return hipGetLastError();
   }
   LaunchTimer timer(label, st);

@@ -154,8 +154,12 @@ def test_workspace_never_scales_with_d_out_times_d_in():
         assert norm_ws < dense / 3
         # at most 16 split-K partial Gram matrices and 16 partial projections P [d_out, r]
         assert norm_ws <= 16 * r * r * 4 + r * r * 4 + 16 * d_out * r * 4 + 4096
-        # forward adds xs [T, r] and split-K partials of at most 16 [T, r] float32 blocks
-        assert fwd_ws - norm_ws <= T * r * 2 + 16 * T * r * 4 + 4096
+        # forward adds xs [T, r] and one split-K region: at most 16 [T, r] float32 blocks
+        # (the down-projection), or, when the fused GEMM's 128 x 128 tiles cannot fill
+        # the chip, its float32 partials: split * tiles <= 384 + tiles / 2 with
+        # tiles = T d_out / 128^2, i.e. at most (384 * 128^2 + T d_out / 2) floats
+        fused_k = 4 * (384 * 128 * 128 + T * d_out // 2)
+        assert fwd_ws - norm_ws <= T * r * 2 + max(16 * T * r * 4, fused_k) + 4096
         split_k = 16 * max(T * r, d_out * r, r * d_in) * 4
         assert bwd_ws <= T * d_out * 2 + 2 * T * r * 2 + ((T + 63) // 64) * d_out * 4 + split_k + 4096
         sep = _lib.shape(d_out, d_in, r, T, _lib.BF16, 2.0, _lib.FLAG_SEPARATE_COMPOSE)
