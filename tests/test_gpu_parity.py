@@ -144,6 +144,9 @@ SMALL = [
     ("sneg_f32", LayerShape(136, 200, 16, 9, -0.75, "f32"), 8, {}),
     ("largeB_bf16", LayerShape(264, 520, 24, 37, 2.0, "bf16"), 9, dict(b_std=0.1)),
     ("zeroB_bf16", LayerShape(264, 520, 24, 37, 2.0, "bf16"), 10, dict(zero_b=True)),
+    # r > d_in / 2 and K tails in every segment (d_in, r, d_out not multiples of 64)
+    ("widerank_bf16", LayerShape(1032, 2056, 1016, 260, 2.0, "bf16"), 11, {}),
+    ("widerank_f32", LayerShape(520, 776, 392, 70, 2.0, "f32"), 12, {}),
 ]
 
 
