@@ -48,7 +48,7 @@ WORKLOAD_TAG = "highrank_d8192_r384_t4096"
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the library sources: recorded counter data applies only to this build."""
+    """sha256 over the library sources: recorded counter data applies only to the sources it was taken from."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:

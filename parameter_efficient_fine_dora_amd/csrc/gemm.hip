@@ -639,8 +639,8 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
 // float32 layers: 64x64 tiles, 16-deep K steps, 4x4 outputs per thread.
 template <bool AKC, bool BKC, int EPI>
 __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
-  constexpr int BM = 64, BN = 64, BKF = kBK;   // one 64-deep step per round
-  constexpr int kPer = BM * BKF / 256;          // elements of each operand per thread and round
+  constexpr int BM = 64, BN = 64, BKF = kBK;   // one 64-deep step per pass through LDS
+  constexpr int kPer = BM * BKF / 256;          // elements of each operand per thread and pass
   __shared__ float As[BKF][BM + 4];
   __shared__ float Bs[BKF][BN + 4];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -658,8 +658,8 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
     const int64_t lda = s == 0 ? p.lda[0] : (s == 1 ? p.lda[1] : p.lda[2]);
     const int64_t ldb = s == 0 ? p.ldb[0] : (s == 1 ? p.ldb[1] : p.ldb[2]);
     const int Ks = s == 0 ? p.K[0] : (s == 1 ? p.K[1] : p.K[2]);
-    // Every load of the round is issued before the first LDS store, so a
-    // round costs one memory latency.  Element e of a K-contiguous operand is
+    // Every load of the pass is issued before the first LDS store, so a
+    // pass costs one memory latency.  Element e of a K-contiguous operand is
     // (row e / 64, k e % 64): 64 lanes read one row's 256 contiguous bytes.
     float va[kPer], vb[kPer];
 #pragma unroll
