@@ -27,12 +27,19 @@
  *              float32; each output is rounded once, to nearest even.
  *   Memory     All tensor pointers are DEVICE pointers, 16-byte aligned.  The
  *              caller owns every buffer, including the workspace `ws`; the
- *              library allocates no device memory and keeps no state between
+ *              library allocates no device memory and keeps no data between
  *              calls.  Inputs are read only.  Outputs must not overlap inputs
  *              or each other.
  *   Streams    Work is enqueued on `hip_stream` (a hipStream_t; NULL = the
- *              null stream) and the call returns without synchronising.  Calls
- *              on distinct buffers may be made from several host threads.
+ *              null stream) and the call returns without synchronising.
+ *              dora_forward and dora_backward may fork independent parts to a
+ *              second stream of the library's own (default priority, one per
+ *              host thread and device, created on the first call and kept
+ *              until the process ends) and join it back through events before
+ *              returning: all work of a call is ordered before anything the
+ *              caller enqueues on `hip_stream` afterwards, and the pattern is
+ *              valid under stream capture.  Calls on distinct buffers may be
+ *              made from several host threads.
  *   Errors     Arguments are validated before anything is enqueued; on a
  *              validation error nothing is written.  Return value 0 = enqueued,
  *              negative = DORA_ERR_* below.  DORA_ERR_HIP means the HIP runtime
