@@ -236,16 +236,118 @@ struct CopyMC {
   }
 };
 
+// M/N-contiguous operand copied straight into LDS (buffer_load ... lds) in
+// its own k-major layout: a stage is 64 k-rows of R elements (2R bytes), the
+// 16-byte chunks of k-row k XOR-swizzled by 4*(k % 4).  One wave instruction
+// fills 1 KiB = kKPI k-rows; lane l takes k-row l / kLPR and physical chunk
+// l % kLPR.  The MFMA fragments are then read with the transposing LDS read
+// (ds_read_b64_tr_b16, see tr_frag); the swizzle spreads the four k-rows one
+// 16-lane group of that read touches over distinct banks.  Columns past the
+// operand carry kOob from the start; k-rows past K are masked on a segment's
+// last step only.
+template <int R, int NW>
+struct CopyNC {
+  static constexpr int kRowB = R * 2;        // bytes of one k-row
+  static constexpr int kLPR = kRowB / 16;    // lanes (16-byte chunks) per k-row
+  static constexpr int kKPI = 64 / kLPR;     // k-rows per wave instruction
+  static constexpr int kInstr = kBK / kKPI / NW;
+  static_assert(kLPR >= 16 && kBK % (kKPI * NW) == 0, "k-rows must split evenly over the waves");
+  Rsrc rs;
+  const uint16_t* base;    // column row0, k = 0
+  int64_t ld;
+  int kt_base;             // step the descriptor starts at
+  int kt_span;             // steps one descriptor covers with a 31-bit scalar offset
+  uint32_t off[kInstr];    // k-row * ld * 2 + logical chunk * 16, or kOob
+  __device__ __forceinline__ static int krow_of(int i, int wave, int lane) {
+    return (wave + i * NW) * kKPI + lane / kLPR;
+  }
+  __device__ __forceinline__ void prepare(const uint16_t* p, int64_t ldv, int row0, int nrows,
+                                          int K, int wave, int lane, int) {
+    base = p + row0;
+    ld = ldv;
+    kt_base = 0;
+    kt_span = (int)((int64_t)0x40000000 / (ldv * 2 * kBK));   // >= 2: ld < 2^22
+    rs = make_rsrc(base, (int64_t)K * ldv * 2);
+#pragma unroll
+    for (int i = 0; i < kInstr; ++i) {
+      const int kr = krow_of(i, wave, lane);
+      const int lc = (lane % kLPR) ^ (4 * (kr & 3));
+      off[i] = row0 + lc * 8 < nrows ? (uint32_t)kr * (uint32_t)(ldv * 2) + (uint32_t)lc * 16u
+                                     : kOob;
+    }
+  }
+  template <bool TAIL>
+  __device__ __forceinline__ void issue(uint8_t* lds_tile, int kt, int K, int wave, int lane,
+                                        int) {
+    if (kt - kt_base >= kt_span) {   // keep the scalar offset below 2^30
+      kt_base = kt;
+      rs = make_rsrc(base + (int64_t)kt * kBK * ld, (int64_t)(K - kt * kBK) * ld * 2);
+    }
+    const int soff = (kt - kt_base) * kBK * (int)(ld * 2);   // < 2^30
+#pragma unroll
+    for (int i = 0; i < kInstr; ++i) {
+      uint32_t o = off[i];
+      if (TAIL && kt * kBK + krow_of(i, wave, lane) >= K) o = kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds_tile + (wave + i * NW) * 1024), 16,
+          (int)o, soff, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void commit(uint8_t*, int) {}
+};
+
+// Byte offset, within a stage of CopyNC's layout (row_bytes per k-row), of the
+// 8-byte piece this lane hands to ds_read_b64_tr_b16 for the 32-row block at
+// blk_row0, 16-deep step 0, first k quad.  A 16-lane group g of that read
+// gathers a 4 (k) x 16 (rows) block: lane 4j + q supplies k-row j, rows 4q..4q+3,
+// and lane i receives row i at the four k.  Lanes 0-15 / 16-31 take rows
+// 0-15 / 16-31 of the block at k 0-7, lanes 32-63 the same rows at k 8-15,
+// which is the operand layout of v_mfma_f32_32x32x16_bf16.  Step kk and the
+// second k quad add (16 kk + 4) * row_bytes; (k-row % 4) stays the lane's j.
+__device__ __forceinline__ int tr_base(int blk_row0, int row_bytes, int lane) {
+  const int g = lane >> 4, jq = lane & 15, j = jq >> 2, q = jq & 3;
+  const int kr = 8 * (g >> 1) + j;
+  const int c = blk_row0 + 16 * (g & 1) + 4 * q;   // first row (column element) of the piece
+  const int pc = (c >> 3) ^ (4 * j);
+  return kr * row_bytes + pc * 16 + ((c >> 2) & 1) * 8;
+}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+// Fragment of 8 consecutive k (two transposing reads, k quads 0 and 1).
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t* p, int row_bytes) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p + 4 * row_bytes));
+  const v4i16 v8[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v8);
+}
+
+#ifndef DORA_MC_DIRECT
+#define DORA_MC_DIRECT 1
+#endif
+
 template <int R, int NT, bool KC>
 struct CopyOp;
 template <int R, int NT>
 struct CopyOp<R, NT, true> : CopyKC<R, NT / 64> {
   static constexpr bool kRegs = false;
+  static constexpr bool kTr = false;
+};
+// Transposed operands go straight to LDS (read back transposed) when the tile
+// has at least 128 rows; narrower tiles stage them through registers.
+template <int R, int NT, bool DIRECT = (DORA_MC_DIRECT && R >= 128)>
+struct CopyOpMC;
+template <int R, int NT>
+struct CopyOpMC<R, NT, true> : CopyNC<R, NT / 64> {
+  static constexpr bool kRegs = false;
+  static constexpr bool kTr = true;
 };
 template <int R, int NT>
-struct CopyOp<R, NT, false> : CopyMC<R, NT> {
+struct CopyOpMC<R, NT, false> : CopyMC<R, NT> {
   static constexpr bool kRegs = true;
+  static constexpr bool kTr = false;
 };
+template <int R, int NT>
+struct CopyOp<R, NT, false> : CopyOpMC<R, NT> {};
 
 // Tile index -> (tile_m, tile_n), XCD-grouped, 8 tile-rows per group (an XCD's
 // 32 CUs then hold an ~8 x 4 block of tiles and share its operand panels in L2).
@@ -307,11 +409,13 @@ __device__ __forceinline__ void wait_vmem_le() {
 }
 
 // Epilogue shared by the bf16 kernels: scale (and compose), then store.  bf16
-// outputs are staged through LDS so that every store is a whole 16-byte piece
-// of a row; float32 outputs (split-K partials) go straight out.
+// outputs are staged through LDS, one 32-row block of the wave's tile at a
+// time in a region of its own (`stg`, 32 x (TN + 8) elements), so that every
+// store is a whole 16-byte piece of a row; float32 outputs (split-K partials)
+// go straight out.
 template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
 __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
-                                              uint8_t* smem, void* c, int64_t ldc,
+                                              uint16_t* stg, void* c, int64_t ldc,
                                               int64_t split_stride, float alpha, const void* mag,
                                               const float* nrm, const void* add, int64_t ld_add,
                                               int M, int N, int m0, int n0, int wave, int wm,
@@ -324,59 +428,58 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / W
   void* cbase = OUT_F32 ? (void*)(reinterpret_cast<float*>(c) + blockIdx.y * split_stride)
                         : (void*)(reinterpret_cast<uint16_t*>(c) + blockIdx.y * split_stride);
   if constexpr (!OUT_F32) {
-    // Stage the wave's tile in LDS (the K loop ended on a barrier, so every
-    // stage is free), then write whole 16-byte pieces of contiguous rows.
-    uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave * TM * kStageLd;
-    float grow[MB];   // merge: g of each of the lane's rows
+    // The K loop ended on a barrier, so every stage is free.  A wave's LDS
+    // accesses complete in order, so block i + 1 may overwrite what block i
+    // read back without a wait.
+    f32x4 gm1[NB][4];   // compose: g - 1 of the lane's columns
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int m = m0 + wm * TM + i * 32 + (lane & 31);
-      grow[i] = (EPI == kEpiMerge && m < M) ? g_row<true>(mag, nrm, m) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int nl = j * 32 + g * 8 + (lane >> 5) * 4;
-        const int n = n0 + wn * TN + nl;
-        f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
-        if (EPI == kEpiCompose && n < N) gm1 = gm1_4<true>(mag, nrm, n);
-        u32x2 w[MB];   // merge: the addend's four values at (row, n..n+3)
+        const int n = n0 + wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
+        gm1[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (EPI == kEpiCompose && n < N) gm1[j][g] = gm1_4<true>(mag, nrm, n);
+      }
+    constexpr int kChunksPerRow = TN / 8;
 #pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const int m = m0 + wm * TM + i * 32 + (lane & 31);
-          w[i] = u32x2{0u, 0u};
+    for (int i = 0; i < MB; ++i) {
+      const int mrow = m0 + wm * TM + i * 32;
+      const int m = mrow + (lane & 31);
+      const float grow = (EPI == kEpiMerge && m < M) ? g_row<true>(mag, nrm, m) : 0.f;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nl = j * 32 + g * 8 + (lane >> 5) * 4;
+          const int n = n0 + wn * TN + nl;
+          u32x2 w = u32x2{0u, 0u};   // merge: the addend's four values at (m, n..n+3)
           if (EPI == kEpiMerge && m < M && n < N)
-            w[i] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(add) +
-                                                   (int64_t)m * ld_add + n);
-        }
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const int ml = i * 32 + (lane & 31);
+            w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(add) +
+                                                (int64_t)m * ld_add + n);
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float z = alpha * acc[i][j][g * 4 + e];
             if (EPI == kEpiMerge) {
-              const uint32_t wv = w[i][e >> 1];
-              v[e] = grow[i] * ((e & 1 ? bf_hi(wv) : bf_lo(wv)) + z);
+              const uint32_t wv = w[e >> 1];
+              v[e] = grow * ((e & 1 ? bf_hi(wv) : bf_lo(wv)) + z);
             } else {
-              v[e] = (EPI == kEpiCompose) ? z + gm1[e] * z : z;
+              v[e] = (EPI == kEpiCompose) ? z + gm1[j][g][e] * z : z;
             }
           }
-          *reinterpret_cast<u32x2*>(stg + ml * kStageLd + nl) =
+          *reinterpret_cast<u32x2*>(stg + (lane & 31) * kStageLd + nl) =
               u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
       }
-    }
-    constexpr int kChunksPerRow = TN / 8;
-#pragma unroll 4
-    for (int c = lane; c < TM * kChunksPerRow; c += 64) {
-      const int row = c / kChunksPerRow, ch = c - row * kChunksPerRow;
-      const int m = m0 + wm * TM + row, n = n0 + wn * TN + ch * 8;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(stg + row * kStageLd + ch * 8);
-      if (m < M && n < N)
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(cbase) + (int64_t)m * ldc + n) = val;
+#pragma unroll
+      for (int c = lane; c < 32 * kChunksPerRow; c += 64) {
+        const int row = c / kChunksPerRow, ch = c - row * kChunksPerRow;
+        const int mm = mrow + row, n = n0 + wn * TN + ch * 8;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(stg + row * kStageLd + ch * 8);
+        if (mm < M && n < N)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(cbase) + (int64_t)mm * ldc + n) =
+              val;
+      }
     }
     return;
   }
@@ -415,21 +518,33 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MB = TM / 32, NB = TN / 32;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  // LDS: [A stage 0 | A stage 1 | B stage 0 | B stage 1], so that every fragment
-  // read is a per-lane base plus an offset that fits the 16-bit immediate.
-  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
-  constexpr int BBASE = 2 * ABYTES;
-  static_assert(ABYTES + (MB > 2 ? 64 * kRowBytes : 0) < 65536 &&
-                    BBYTES + (NB > 2 ? 64 * kRowBytes : 0) < 65536,
-                "stage offsets must fit the LDS immediate");
-  constexpr int kStageLd = TN + 8;
-  constexpr int kOutBytes = OUT_F32 ? 0 : NW * TM * kStageLd * 2;
-  constexpr int kSmem = 2 * (ABYTES + BBYTES) > kOutBytes ? 2 * (ABYTES + BBYTES) : kOutBytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
   using CA = CopyOp<BM, NT, AKC>;
   using CB = CopyOp<BN, NT, BKC>;
   constexpr bool kRegs = CA::kRegs || CB::kRegs;
-
+  constexpr bool kTrA = CA::kTr, kTrB = CB::kTr;
+  // LDS.  With an operand read by the transposing read, one object per operand
+  // and stage: kept apart, they let the compiler see that a stage's fragment
+  // reads cannot touch the other stage, which the copies in flight are
+  // filling (without that it waits for every copy before a transposing read).
+  // Otherwise one object [A stage 0 | A stage 1 | B stage 0 | B stage 1], so
+  // that every fragment read is a per-lane base plus an immediate offset.
+  constexpr bool kSplit = kTrA || kTrB;
+  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
+  constexpr int BBASE = kSplit ? 0 : 2 * ABYTES;   // B's offset within its object
+  static_assert(kSplit || (ABYTES + (MB > 2 ? 64 * kRowBytes : 0) < 65536 &&
+                           BBYTES + (NB > 2 ? 64 * kRowBytes : 0) < 65536),
+                "stage offsets must fit the LDS immediate");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSplit ? ABYTES : 2 * (ABYTES + BBYTES)];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kSplit ? ABYTES : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kSplit ? BBYTES : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[kSplit ? BBYTES : 1];
+  // bf16 epilogue: each wave stages 32 rows of its tile at a time in a region
+  // of its own.
+  constexpr int kStageLd = TN + 8;
+  constexpr int kStgBytes = 32 * kStageLd * 2;
+  static_assert(OUT_F32 || (kSplit ? ((NW + 3) / 4) * kStgBytes <= (ABYTES < BBYTES ? ABYTES : BBYTES)
+                                   : NW * kStgBytes <= 2 * (ABYTES + BBYTES)),
+                "epilogue staging must fit the stage objects");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
@@ -473,12 +588,29 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
       ra[par][kk] = (uint32_t)(rowa * kRowBytes + ((ch ^ swz(rowa)) << 4));
       rb[par][kk] = (uint32_t)(BBASE + rowb * kRowBytes + ((ch ^ swz(rowb)) << 4));
     }
+  // Operands kept k-major in LDS are read with the transposing read: one base
+  // per 32-row block (the chunk swizzle mixes the block index with the k-row).
+  static_assert(52 * BM * 2 < 65536 && 52 * BN * 2 < 65536,
+                "transposing-read offsets must fit the LDS immediate");
+  uint32_t ta[kTrA ? MB : 1], tb[kTrB ? NB : 1];
+  if constexpr (kTrA) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) ta[i] = (uint32_t)tr_base(wm * TM + i * 32, BM * 2, lane);
+  }
+  if constexpr (kTrB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) tb[j] = (uint32_t)tr_base(wn * TN + j * 32, BN * 2, lane);
+  }
 
+  // Stage SB of each operand (B's offset BBASE within the object is in the
+  // fragment bases and added for the copies).
+#define DORA_A(SB) (kSplit ? ((SB) ? sA1 : smem) : smem + (SB) * ABYTES)
+#define DORA_B(SB) (kSplit ? ((SB) ? sB1 : sB0) : smem + (SB) * BBYTES)
   // Copies of segment step KR into stage SB.
 #define DORA_FETCH(KR, SB)                                                                 \
   do {                                                                                     \
-    uint8_t* sa_ = smem + (SB) * ABYTES;                                                   \
-    uint8_t* sb_ = smem + BBASE + (SB) * BBYTES;                                           \
+    uint8_t* sa_ = DORA_A(SB);                                                             \
+    uint8_t* sb_ = DORA_B(SB) + BBASE;                                                     \
     if (partial && (KR) == last) {                                                         \
       ca.template issue<true>(sa_, (KR), Ks, wave, lane, tid);                             \
       cb.template issue<true>(sb_, (KR), Ks, wave, lane, tid);                             \
@@ -492,20 +624,30 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   do {                                                                                     \
     if (kRegs) {                                                                           \
       wait_vmem();                                                                         \
-      ca.commit(smem + (SB) * ABYTES, tid);                                                \
-      cb.commit(smem + BBASE + (SB) * BBYTES, tid);                                        \
+      ca.commit(DORA_A(SB), tid);                                                          \
+      cb.commit(DORA_B(SB) + BBASE, tid);                                                  \
     }                                                                                      \
   } while (0)
 
   bf16x8 af[2][MB], bfr[2][NB];
 #define DORA_READ(SET, SB, KK)                                                             \
   do {                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < MB; ++i) af[SET][i] =                            \
-        *reinterpret_cast<const bf16x8*>(smem + ra[i & 1][KK] + (i >> 1) * 64 * kRowBytes + \
-                                         (SB) * ABYTES);                                   \
-    _Pragma("unroll") for (int j = 0; j < NB; ++j) bfr[SET][j] =                           \
-        *reinterpret_cast<const bf16x8*>(smem + rb[j & 1][KK] + (j >> 1) * 64 * kRowBytes + \
-                                         (SB) * BBYTES);                                   \
+    if constexpr (kTrA) {                                                                  \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) af[SET][i] =                          \
+          tr_frag(DORA_A(SB) + ta[i] + (KK) * 16 * BM * 2, BM * 2);                        \
+    } else {                                                                               \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) af[SET][i] =                          \
+          *reinterpret_cast<const bf16x8*>(DORA_A(SB) + ra[i & 1][KK] +                    \
+                                           (i >> 1) * 64 * kRowBytes);                     \
+    }                                                                                      \
+    if constexpr (kTrB) {                                                                  \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j) bfr[SET][j] =                         \
+          tr_frag(DORA_B(SB) + tb[j] + (KK) * 16 * BN * 2, BN * 2);                        \
+    } else {                                                                               \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j) bfr[SET][j] =                         \
+          *reinterpret_cast<const bf16x8*>(DORA_B(SB) + rb[j & 1][KK] +                    \
+                                           (j >> 1) * 64 * kRowBytes);                     \
+    }                                                                                      \
   } while (0)
   // One stage: four 16-deep steps, fragments of step kk+1 read during step kk.
 #define DORA_MMA(SB, SQ)                                                                   \
@@ -582,6 +724,8 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
 #undef DORA_COMMIT
 #undef DORA_READ
 #undef DORA_MMA
+#undef DORA_A
+#undef DORA_B
 
   if constexpr (kRowSq) {
     // Lane l and lane l + 32 hold the two halves of every 16-deep step of
@@ -631,7 +775,12 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
     return;
   }
 
-  gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, smem, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
+  uint8_t* const stg_obj =
+      !kSplit ? smem + wave * kStgBytes
+              : ((wave & 3) == 0 ? smem : (wave & 3) == 1 ? sA1 : (wave & 3) == 2 ? sB0 : sB1) +
+                    (wave >> 2) * kStgBytes;
+  uint16_t* const stg = reinterpret_cast<uint16_t*>(stg_obj);
+  gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, stg, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
                                                 p.norm, p.add, p.ld_add, M, N, m0, n0, wave, wm,
                                                 wn, lane);
 }
