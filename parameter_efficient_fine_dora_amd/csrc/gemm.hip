@@ -349,18 +349,28 @@ struct CopyOpMC<R, NT, false> : CopyMC<R, NT> {
 template <int R, int NT>
 struct CopyOp<R, NT, false> : CopyOpMC<R, NT> {};
 
-// Tile index -> (tile_m, tile_n), XCD-grouped, 8 tile-rows per group (an XCD's
-// 32 CUs then hold an ~8 x 4 block of tiles and share its operand panels in L2).
-// Returns tile_m in .x and tile_n in .y.
+// Tile index -> (tile_m, tile_n), XCD-grouped.  The hardware deals workgroups
+// to the 8 XCDs round robin; the index is remapped so that each XCD takes a
+// contiguous run, and runs walk groups of tile-rows column by column, so an
+// XCD's tiles form a block whose operand panels its L2 shares.  Groups are 8
+// tile-rows (an ~8 x 8 block per XCD on large outputs); when every column of
+// tiles fits in an XCD's run with a block no wider than tall (skinny outputs,
+// such as the rank-r projections), a group is exactly one XCD's run, so each
+// XCD reads every panel of its tile-rows once instead of spilling half a group
+// onto the next XCD.  Returns tile_m in .x and tile_n in .y.
 __device__ __forceinline__ int2 tile_coords(int tiles_m, int tiles_n) {
   int L = blockIdx.x;
   const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) L = (L & 7) * (nwg >> 3) + (L >> 3);
-  constexpr int kGroup = 8;
-  const int per_group = kGroup * tiles_n;
+  int group = 8;
+  if ((nwg & 7) == 0) {
+    L = (L & 7) * (nwg >> 3) + (L >> 3);
+    const int run = nwg >> 3;
+    if (tiles_n * tiles_n <= run && run % tiles_n == 0) group = run / tiles_n;
+  }
+  const int per_group = group * tiles_n;
   const int g = L / per_group;
-  const int first = g * kGroup;
-  const int gsz = min(tiles_m - first, kGroup);
+  const int first = g * group;
+  const int gsz = min(tiles_m - first, group);
   const int rem = L - g * per_group;
   return make_int2(first + rem % gsz, rem / gsz);
 }
