@@ -219,80 +219,59 @@ __global__ __launch_bounds__(256) void dora_compose_fwd(void* y, const void* slo
 // This kernel writes gz = g * gy and, per token block b, the column partial
 // sums dm_part[b, i] = sum_{t in b} gy[t,i] y[t,i]; dora_dm_finalize adds the
 // blocks in a fixed order, so the result does not depend on scheduling.
-// A workgroup covers 64 16-byte column vectors of one token block with 4
-// thread rows, each summing a contiguous quarter of the block's tokens; the
-// four row sums are combined through LDS in a fixed order.  (Four waves per
-// token block rather than one keep enough loads in flight per CU to stream at
-// the HBM rate.)
 template <bool BF>
 __global__ __launch_bounds__(256) void dora_compose_bwd(const void* gy, const void* y,
                                                         const void* m, const float* norm, void* gz,
                                                         float* dm_part, int64_t T, int64_t d_out,
                                                         int64_t tok_per_block) {
   using V = Vec<BF>;
-  constexpr int kN = V::kN;
-  __shared__ float red[4][kN][64];
-  const int64_t nvec = d_out / kN;
-  const int lane = threadIdx.x & 63, row = threadIdx.x >> 6;
-  const int64_t cv = (int64_t)blockIdx.x * 64 + lane;
-  const bool live = cv < nvec;
-  float g[kN], acc[kN];
+  const int64_t nvec = d_out / V::kN;
+  const int64_t cv = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (cv >= nvec) return;
+  float g[V::kN], acc[V::kN];
 #pragma unroll
-  for (int q = 0; q < kN; ++q) {
-    g[q] = live ? V::scalar(m, cv * kN + q) / fmaxf(norm[cv * kN + q], kNormEps) : 0.f;
+  for (int q = 0; q < V::kN; ++q) {
+    const int64_t col = cv * V::kN + q;
+    g[q] = V::scalar(m, col) / fmaxf(norm[col], kNormEps);
     acc[q] = 0.f;
   }
-  const int64_t quarter = (tok_per_block + 3) / 4;
-  const int64_t tb = (int64_t)blockIdx.y * tok_per_block;
-  const int64_t tb_end = min(T, tb + tok_per_block);
-  const int64_t t0 = min(tb_end, tb + row * quarter);
-  const int64_t t1 = min(tb_end, t0 + quarter);
-  if (live) {
-    constexpr int U = 4;   // tokens in flight per thread
-    int64_t t = t0;
-    for (; t + U <= t1; t += U) {
-      float a[U][kN], b[U][kN];
+  const int64_t t0 = (int64_t)blockIdx.y * tok_per_block;
+  const int64_t t1 = min(T, t0 + tok_per_block);
+  constexpr int U = 4;   // tokens in flight per thread
+  int64_t t = t0;
+  for (; t + U <= t1; t += U) {
+    float a[U][V::kN], b[U][V::kN];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        V::load(gy, (t + u) * nvec + cv, a[u]);
-        V::load(y, (t + u) * nvec + cv, b[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float o[kN];
-#pragma unroll
-        for (int q = 0; q < kN; ++q) {
-          o[q] = g[q] * a[u][q];
-          acc[q] = fmaf(a[u][q], b[u][q], acc[q]);
-        }
-        V::store(gz, (t + u) * nvec + cv, o);
-      }
+    for (int u = 0; u < U; ++u) {
+      V::load(gy, (t + u) * nvec + cv, a[u]);
+      V::load(y, (t + u) * nvec + cv, b[u]);
     }
-    for (; t < t1; ++t) {
-      float a[kN], b[kN], o[kN];
-      V::load(gy, t * nvec + cv, a);
-      V::load(y, t * nvec + cv, b);
 #pragma unroll
-      for (int q = 0; q < kN; ++q) {
-        o[q] = g[q] * a[q];
-        acc[q] = fmaf(a[q], b[q], acc[q]);
+    for (int u = 0; u < U; ++u) {
+      float o[V::kN];
+#pragma unroll
+      for (int q = 0; q < V::kN; ++q) {
+        o[q] = g[q] * a[u][q];
+        acc[q] = fmaf(a[u][q], b[u][q], acc[q]);
       }
-      V::store(gz, t * nvec + cv, o);
+      V::store(gz, (t + u) * nvec + cv, o);
     }
   }
+  for (; t < t1; ++t) {
+    float a[V::kN], b[V::kN], o[V::kN];
+    V::load(gy, t * nvec + cv, a);
+    V::load(y, t * nvec + cv, b);
 #pragma unroll
-  for (int q = 0; q < kN; ++q) red[row][q][lane] = acc[q];
-  __syncthreads();
-  if (row == 0 && live) {
-    float sum[kN];
-#pragma unroll
-    for (int q = 0; q < kN; ++q)
-      sum[q] = (red[0][q][lane] + red[1][q][lane]) + (red[2][q][lane] + red[3][q][lane]);
-    float* dst = dm_part + (int64_t)blockIdx.y * d_out + cv * kN;
-#pragma unroll
-    for (int q = 0; q < kN; q += 4)
-      *reinterpret_cast<f32x4*>(dst + q) = f32x4{sum[q], sum[q + 1], sum[q + 2], sum[q + 3]};
+    for (int q = 0; q < V::kN; ++q) {
+      o[q] = g[q] * a[q];
+      acc[q] = fmaf(a[q], b[q], acc[q]);
+    }
+    V::store(gz, t * nvec + cv, o);
   }
+  float* dst = dm_part + (int64_t)blockIdx.y * d_out + cv * V::kN;
+#pragma unroll
+  for (int q = 0; q < V::kN; q += 4)
+    *reinterpret_cast<f32x4*>(dst + q) = f32x4{acc[q], acc[q + 1], acc[q + 2], acc[q + 3]};
 }
 
 // 64 columns per workgroup, the partial blocks split over 4 thread rows and
@@ -562,7 +541,7 @@ hipError_t compose_bwd(const void* gy, const void* y, const void* m, const float
   if (T <= 0) return hipSuccess;
   LaunchTimer t("compose_bwd", st);
   const int64_t vec = dtype == kBF16 ? 8 : 4;
-  const dim3 grid((unsigned)cdiv(d_out / vec, 64), (unsigned)cdiv(T, tokens_per_block));
+  const dim3 grid((unsigned)cdiv(d_out / vec, 256), (unsigned)cdiv(T, tokens_per_block));
   if (dtype == kBF16)
     hipLaunchKernelGGL(dora_compose_bwd<true>, grid, dim3(256), 0, st, gy, y, m, norm, gz, dm_part,
                        T, d_out, tokens_per_block);
