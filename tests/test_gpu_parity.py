@@ -246,6 +246,38 @@ def test_fullsize_backward_sampled(ops):
     check_out(got["dm"][rows], ref["dm"], "dm (sampled rows)")
 
 
+def test_long_batch_rebased_copies(ops):
+    """A long token batch, T * d_out > 2^29: gz and x, the transposed operands of the
+    dB and dA products, each span more than 1 GiB.  A buffer copy carries 32-bit
+    offsets, so the copiers move their descriptor forward inside a launch (here at
+    step 8192 of 10241, in the splits that reach it); ragged T checks the last step."""
+    shape = LayerShape(1024, 1024, 64, 655397, 2.0, "bf16")
+    assert shape.tokens * shape.d_out * 2 > 1 << 30
+    say(f"long batch T={shape.tokens}")
+    layer = synth.make_layer(shape, 71, grad=True)
+    dev = layer_to_device(layer, "bf16")
+    y, norm, xs = ops.dora_forward(dev["x"], dev["W0"], dev["A"], dev["B"], dev["m"], shape.s)
+    gx, gA, gB, gm = ops.dora_backward(dev["gy"], dev["x"], dev["W0"], dev["A"], dev["B"], dev["m"],
+                                       norm, xs, y, shape.s)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(72))
+    tok = np.unique(np.concatenate([_sample(rng, shape.tokens, 48), [shape.tokens - 1]]))
+    rows = np.unique(np.concatenate([_sample(rng, shape.d_out, 64), [shape.d_out - 1]]))
+    cols = np.unique(np.concatenate([_sample(rng, shape.d_in, 64), [shape.d_in - 1]]))
+    got_dx = download(gx[torch.from_numpy(tok).cuda()])
+    got_dB, got_dA, got_dm = download(gB), download(gA), download(gm)
+    del dev, y, xs, gx, gA, gB, gm
+    torch.cuda.empty_cache()
+    L = {k: synth.to_f64(v, "bf16") for k, v in layer.items()}
+    del layer
+    ref = oracle.dora_backward_sampled(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s,
+                                       tok, rows, cols)
+    check_out(got_dx, ref["dx"], "dx (sampled tokens)")
+    check_out(got_dB[rows], ref["dB"], "dB (sampled rows)")
+    check_out(got_dA[:, cols], ref["dA"], "dA (sampled columns)")
+    check_out(got_dm[rows], ref["dm"], "dm (sampled rows)")
+
+
 # ---- the three norm terms, separated by flipping B ------------------------------------
 
 def test_norm_terms_separately(ops):
