@@ -973,7 +973,8 @@ hipError_t launch_layout(bool akc, bool bkc, const KArgs& a, int epi, bool out_f
   if (akc && bkc) return launch_bf16<BM, BN, WM, WN, true, true>(a, epi, out_f32, grid, st);
   if (akc && !bkc) return launch_bf16<BM, BN, WM, WN, true, false>(a, epi, out_f32, grid, st);
   // two register-staged operands do not fit beside a 256 x 256 tile's accumulators
-  if constexpr (BM * BN <= 256 * 128)
+  // (transposed operands of 128 rows or more are copied straight to LDS)
+  if constexpr (BM * BN <= 256 * 128 || (DORA_MC_DIRECT && BM >= 128 && BN >= 128))
     if (!akc && !bkc) return launch_bf16<BM, BN, WM, WN, false, false>(a, epi, out_f32, grid, st);
   return hipErrorInvalidValue;
 }
@@ -1068,10 +1069,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bk
     return {-1, (int)std::max<int64_t>(1, std::min<int64_t>(split, 16))};
   }
   auto tiles = [&](int cfg) { return cdiv64(M, kCfgs[cfg].bm) * cdiv64(N, kCfgs[cfg].bn); };
-  const bool both_mc = !akc && !bkc;
   // Large outputs: 256 x 256 tiles (8 waves), then 256 x 128 (8 waves).  Two
-  // transposed operands take the 256 x 128 tile (register budget).
-  if (!both_mc && tiles(0) >= 256) return {0, 1};
+  // transposed operands take the large tile only when they are copied straight
+  // to LDS (two register-staged ones would not fit beside its accumulators).
+  const bool both_mc = !akc && !bkc;
+  if ((DORA_MC_DIRECT || !both_mc) && tiles(0) >= 256) return {0, 1};
   if (tiles(5) >= 256) return {5, 1};   // only when it still fills every CU
   // Skinny or small, split along K: 128 x 128 tiles at ~384 workgroups did best
   // for every operand layout of the d = 8192, r = 384 layer (xs, P, ts, dB, dA).

@@ -161,6 +161,17 @@ def test_small_parity(ops, name, shape, seed, kw, flags):
         assert not got["dA"].any(), "B = 0 gives dA = 0 exactly"
 
 
+def test_fullrank_large_tile_transposed_products(ops):
+    """r close to d: the dB (d_out x r) and dA (r x d_in) products have 272 output
+    tiles each, enough for the 256 x 256 tile with both operands transposed; every
+    dimension is ragged against it and K = T = 333 ends on a partial step."""
+    shape = LayerShape(4104, 4104, 4040, 333, 2.0, "bf16")
+    say(f"full-rank large-tile parity shape={shape}")
+    layer = synth.make_layer(shape, 13, grad=True)
+    got = run_layer(ops, shape, layer)
+    compare_full(shape, layer, got)
+
+
 def test_skip_outputs_and_recompute_xs(ops):
     shape = LayerShape(264, 520, 24, 37, 2.0, "bf16")
     layer = synth.make_layer(shape, 11, grad=True)
