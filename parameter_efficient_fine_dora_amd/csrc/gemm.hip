@@ -12,12 +12,15 @@
 // 16-byte chunks whose order is XOR-swizzled by the row index
 // ((row & 7) ^ ((row >> 3) & 7)) so that the eight (and sixteen) rows a
 // 16-byte-per-lane read or write touches land in distinct bank groups.
-// K-contiguous operands go global -> LDS directly (buffer_load ... lds);
-// M/N-contiguous operands are loaded as 4(k) x 8(m) bf16 blocks and
-// transposed in registers before the store, so the MFMA fragment reads are
-// the same for both.  Each wave computes a (BM/WM) x (BN/WN) sub-tile of
-// 32x32 MFMA blocks.  The MFMA runs as D = opB-tile x opA-tile^T so that every
-// lane ends up holding four consecutive output columns.
+// Both operand layouts go global -> LDS directly (buffer_load ... lds).
+// K-contiguous operands keep their rows and are read with ds_read_b128;
+// M/N-contiguous operands keep their k-major layout (chunks swizzled by the
+// k-row instead) and are read with the transposing ds_read_b64_tr_b16, which
+// yields the same MFMA fragments.  (Tiles narrower than 128 rows transpose
+// M/N-contiguous operands in registers instead.)  Each wave computes a
+// (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  The MFMA runs as
+// D = opB-tile x opA-tile^T so that every lane ends up holding four
+// consecutive output columns.
 //
 // Instruction budget.  With eight waves per CU every scalar or vector
 // instruction of the K loop competes with the MFMA issue, so the loop holds
@@ -28,7 +31,8 @@
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 // remapped so that consecutive tiles (which share operand panels) run on
-// one XCD and share its L2, and tiles are walked in groups of 8 tile-rows.
+// one XCD and share its L2, and tiles are walked in groups of tile-rows sized
+// so that each XCD holds a compact block (tile_coords).
 #include <algorithm>
 
 #include "kernels.h"
@@ -321,6 +325,8 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint8_t* p, int row_bytes) {
   return __builtin_bit_cast(bf16x8, v8);
 }
 
+// Build switch: 0 stages every M/N-contiguous operand through registers
+// (the earlier path, kept so the two can be timed against each other).
 #ifndef DORA_MC_DIRECT
 #define DORA_MC_DIRECT 1
 #endif
