@@ -332,6 +332,20 @@ def main():
         torch.cuda.synchronize()
         ms_per_step = ev0.elapsed_time(ev1) / args.steps
     wall = time.perf_counter() - t0
+    if not args.cold:
+        # the spread: the same number of steps again, each bracketed by its own
+        # events (outside the timed region; `value` stays the bracketed mean)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record()
+            run()
+            b.record()
+        torch.cuda.synchronize()
+        per = [a.elapsed_time(b) for a, b in evs]
+    step_stats = {"median_us": round(float(np.median(per)) * 1e3, 2),
+                  "min_us": round(float(np.min(per)) * 1e3, 2),
+                  "max_us": round(float(np.max(per)) * 1e3, 2), "n": len(per)}
 
     # per-kernel times: the same steps again, each launch bracketed by HIP events
     print("# per-kernel timing", file=sys.stderr, flush=True)
@@ -390,7 +404,8 @@ def main():
     rec = {
         "metric": metric, "value": round(ms_per_step * 1e3, 2), "unit": "us",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4), "higher_is_better": False, "scaling": "weak",
+        "ms_per_step": round(ms_per_step, 4), "step_spread": step_stats,
+        "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": shape.dtype, "data": "synthetic",
         "config": {"workload": f"{workload}, {shape.dtype}", "name": args.config,
                    "d_out": d_out, "d_in": d_in, "r": r, "tokens": T, "s": s,
