@@ -234,8 +234,11 @@ def test_fullsize_forward_sampled(ops, name):
         del got
 
 
-def test_fullsize_backward_sampled(ops):
-    name = "highrank_bwd_bf16"
+@pytest.mark.parametrize("name", ["highrank_bwd_bf16", "widemlp_bf16"])
+def test_fullsize_backward_sampled(ops, name):
+    """The backward at full size on sampled tokens, rows and columns: the 8192 x 8192
+    (r 384) layer of the headline step and the 27648 x 5120 (r 256, T 8192) one,
+    whose d_out != d_in and long K = d_out + r in dx."""
     shape = synth.CONFIGS[name]
     say(f"full-size backward {name}")
     layer = synth.make_layer(shape, synth.CONFIG_SEED[name], grad=True)
