@@ -1,0 +1,75 @@
+"""bench.py's host-side contract, without a GPU: the one-GPU exit, the
+algorithmic work model, the per-kernel roofline arithmetic and the guard that
+ties recorded counter data to the kernel sources it was taken from."""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode != 0
+    assert "one GPU" in (res.stdout + res.stderr)
+
+
+def test_algorithmic_work_closed_forms():
+    d, r, T = 8192, 384, 4096
+    w = bench.algorithmic_work(d, d, r, T)
+    # the two large contractions of the step: [x | xs] [W0 | B]^T and [gz | ts] [W0 ; A]
+    assert w["fused_fwd_gemm"] == ("flop", 2 * T * d * (d + r))
+    assert w["dx_gemm"] == ("flop", 2 * T * d * (d + r))
+    assert w["fused_fwd_gemm"][1] == 575_525_617_664
+    # the rank-r products: one multiply-add per (row, column, k)
+    for k in ("down_proj_xs", "t_proj", "dB_gemm", "dA_gemm"):
+        assert w[k] == ("flop", 2 * T * d * r), k
+    # the compose backward reads gy and y, writes gz, and the per-64-token partials
+    kind, nbytes = w["compose_bwd"]
+    assert kind == "byte"
+    assert nbytes == 3 * T * d * 2 + d * (2 + 4) + (T // 64) * d * 4
+    # every entry is a positive amount of a known kind
+    assert all(kind in ("flop", "byte") and amount > 0 for kind, amount in w.values())
+
+
+def test_kernel_table_arithmetic():
+    work = bench.algorithmic_work(8192, 8192, 384, 4096)
+    # two launches of dx totalling 1 ms over 2 steps: 500 us each
+    timing = {"dx_gemm": (2, 1.0), "compose_bwd": (2, 0.07)}
+    table = bench.kernel_table(timing, 2, work, {}, peaks={"mfma_bf16_TFs": 2400.0,
+                                                          "hbm_stream_GBs": 5600.0})
+    dx = table["dx_gemm"]
+    assert dx["launches_per_step"] == 1.0 and dx["avg_us"] == 500.0
+    tf = work["dx_gemm"][1] / 500e-6 / 1e12
+    assert abs(dx["tflops"] - tf) < 0.01
+    assert abs(dx["frac_mfma_peak"] - tf / bench.BF16_PEAK_TFS) < 1e-4
+    assert abs(dx["frac_measured_mfma"] - tf / 2400.0) < 1e-4
+    cb = table["compose_bwd"]
+    gbs = work["compose_bwd"][1] / 35e-6 / 1e9
+    assert abs(cb["gbps"] - gbs) < 0.1
+    assert abs(cb["frac_hbm_peak"] - gbs / bench.HBM_PEAK_GBS) < 1e-4
+
+
+def test_kernel_source_hash_is_stable():
+    h = bench.kernel_source_hash()
+    assert re.fullmatch(r"[0-9a-f]{16}", h)
+    assert bench.kernel_source_hash() == h
+
+
+def test_recorded_traffic_belongs_to_these_sources():
+    """Counter data recorded for other sources is never reported: the traffic
+    table is either empty or carries bytes for the step's kernels."""
+    traffic = bench.recorded_traffic()
+    if not traffic:
+        return
+    assert "dx_gemm" in traffic and "fused_fwd_gemm" in traffic
+    # dx reads at least its operands once (W0, A, gz, ts) and writes dx
+    d, r, T = 8192, 384, 4096
+    floor = (d * d + r * d + T * (d + r) + T * d) * 2
+    assert traffic["dx_gemm"]["total_bytes"] >= floor
