@@ -238,6 +238,36 @@ hipError_t join_from(SideStream* side, hipStream_t st) {
   return hipStreamWaitEvent(st, side->join, 0);
 }
 
+// A fork of `st` to the side stream that is joined back on every way out of
+// the scope: join() on the normal path (its error is reported), the destructor
+// on an early return after a failed launch (the caller's stream is then still
+// ordered after whatever reached the side stream, and a stream capture is not
+// left with an open fork).
+class SideFork {
+ public:
+  SideFork(SideStream* side, hipStream_t st) : side_(side), st_(st) {}
+  SideFork(const SideFork&) = delete;
+  SideFork& operator=(const SideFork&) = delete;
+  ~SideFork() {
+    if (forked_) (void)join_from(side_, st_);
+  }
+  hipStream_t side() const { return side_->s; }
+  hipError_t fork() {
+    forked_ = true;   // a half-made fork (record done, wait failed) is still joined
+    return fork_to(st_, side_);
+  }
+  hipError_t join() {
+    if (!forked_) return hipSuccess;
+    forked_ = false;
+    return join_from(side_, st_);
+  }
+
+ private:
+  SideStream* side_;
+  hipStream_t st_;
+  bool forked_ = false;
+};
+
 // Validation-only op id of calls that take no workspace.
 constexpr int kOpNoWorkspace = -1;
 
@@ -431,13 +461,13 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
     HIP_TRY(gemm(d, dt, on, "down_proj_xs"));
     return DORA_OK;
   };
+  SideFork fk(side, st);
   if (side) {
-    HIP_TRY(fork_to(st, side));
-    DORA_CHECK(down_proj(side->s));
+    HIP_TRY(fk.fork());
+    DORA_CHECK(down_proj(fk.side()));
   }
-  const int rc_norm = run_norm(s, W0, A, B, norm_out, ws, L, st);
-  if (side) HIP_TRY(join_from(side, st));   // joined even if the norm failed
-  DORA_CHECK(rc_norm);
+  DORA_CHECK(run_norm(s, W0, A, B, norm_out, ws, L, st));
+  HIP_TRY(fk.join());
   if (noT) return DORA_OK;
   if (!side && s.r > 0) DORA_CHECK(down_proj(st));
 
@@ -551,12 +581,15 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     }
     return DORA_OK;
   };
+  // columns with m_i == 0 take dm from its definition (y / m = z / n fails there)
+  const DmRecompute zr{norm, grad_y, x, W0, A, B, s.s, s.tokens, s.d_in, s.r};
+  SideFork fk(side, st);
   if (side) {
-    HIP_TRY(fork_to(st, side));
-    if (dm) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, dt, side->s));
-    DORA_CHECK(grad_b(side->s, true, xs));
+    HIP_TRY(fk.fork());
+    if (dm) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, zr, dt, fk.side()));
+    DORA_CHECK(grad_b(fk.side(), true, xs));
   } else if (dm) {
-    HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, dt, st));
+    HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, zr, dt, st));
   }
 
   // A.1 terms: k' = -s m dm / n^2, Bk' = diag(k') B, Q = W0 A^T + s B G,
@@ -686,7 +719,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     give_scratch(a, ws, L);
     HIP_TRY(gemm(a, dt, st, "dA_gemm"));
   }
-  if (side) HIP_TRY(join_from(side, st));
+  HIP_TRY(fk.join());
   return DORA_OK;
 }
 

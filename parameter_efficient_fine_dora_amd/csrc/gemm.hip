@@ -105,14 +105,19 @@ template <int R, int NW>
 struct CopyKC {
   static constexpr int kInstr = R / 8 / NW;   // 16-byte copies per lane and stage
   static_assert(R % (8 * NW) == 0, "rows must split evenly over the waves");
+  static_assert(R <= 256, "R rows of a stride below 2^22 elements must span < 2^31 bytes");
   // Instruction i of a wave fills rows (wave + i*NW)*8 .. +8.  With NW a
   // multiple of 8 every instruction sees the same swizzle, so one per-lane
-  // offset serves them all and the row step goes into the scalar offset.
+  // offset serves them all: on a full tile the row step goes into the scalar
+  // offset.  The hardware range check covers the per-lane offset only (the
+  // scalar offset is added after it), so on a partial tile the row step goes
+  // into the per-lane offset instead and rows past the operand read as zeros.
   static constexpr bool kOne = NW % 8 == 0;
   static constexpr int kOffs = kOne ? 1 : kInstr;
   Rsrc rs;                 // tile base at k = 0, records = valid rows * ld * 2
   uint32_t off[kOffs];     // row * ld * 2 + chunk * 16 (< 2^31: every dimension is < 2^22)
   int step;                // bytes between instruction i and i+1 when kOne
+  bool full;               // kOne: all R rows of the tile lie inside the operand (wave-uniform)
   __device__ __forceinline__ static int row_of(int i, int wave, int lane) {
     return (wave + i * NW) * 8 + (lane >> 3);
   }
@@ -120,6 +125,7 @@ struct CopyKC {
                                           int wave, int lane, int) {
     int64_t rows = nrows - row0;
     if (rows > R) rows = R;
+    full = rows == R;
     rs = make_rsrc(p + (int64_t)row0 * ld, rows * ld * 2);
     step = NW * 8 * (int)(ld * 2);
 #pragma unroll
@@ -132,13 +138,14 @@ struct CopyKC {
   // Step kt (relative to the segment) into the stage tile.  On a partial step
   // the chunks at or beyond K read as zeros: kOob plus the scalar offset stays
   // below 2^32 and beyond every record count.
-  template <bool TAIL>
-  __device__ __forceinline__ void issue(uint8_t* lds_tile, int kt, int K, int wave, int lane,
-                                        int) {
+  template <bool TAIL, bool ROWSTEP_IN_SOFF>
+  __device__ __forceinline__ void issue_rows(uint8_t* lds_tile, int kt, int K, int wave,
+                                             int lane) {
     const int kbytes = kt * kRowBytes;
 #pragma unroll
     for (int i = 0; i < kInstr; ++i) {
-      uint32_t o = off[kOne ? 0 : i];
+      // row * ld * 2 + chunk * 16 < R * 2^23 <= 2^31: the per-lane sum cannot wrap
+      uint32_t o = kOne ? (ROWSTEP_IN_SOFF ? off[0] : off[0] + (uint32_t)(i * step)) : off[i];
       if (TAIL) {
         const int row = row_of(i, wave, lane);
         const int kc = (lane & 7) ^ swz(row);
@@ -146,8 +153,16 @@ struct CopyKC {
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)(lds_tile + (wave + i * NW) * 8 * kRowBytes),
-          16, (int)o, kbytes + (kOne ? i * step : 0), 0, 0);
+          16, (int)o, kbytes + ((kOne && ROWSTEP_IN_SOFF) ? i * step : 0), 0, 0);
     }
+  }
+  template <bool TAIL>
+  __device__ __forceinline__ void issue(uint8_t* lds_tile, int kt, int K, int wave, int lane,
+                                        int) {
+    if (!kOne || full)
+      issue_rows<TAIL, true>(lds_tile, kt, K, wave, lane);
+    else
+      issue_rows<TAIL, false>(lds_tile, kt, K, wave, lane);
   }
   __device__ __forceinline__ void commit(uint8_t*, int) {}
 };

@@ -113,9 +113,18 @@ hipError_t compose_bwd(const void* gy, const void* y, const void* m, const float
                        float* dm_part, int64_t T, int64_t d_out, int64_t tokens_per_block,
                        int dtype, hipStream_t st);
 
-// dm_i = sum_b dm_part[b, i] / m_i (fixed order).
+// What dm_finalize needs to recompute a column whose m_i is zero (where
+// y / m = z / n does not hold): dm_i = sum_t gy[t,i] (x_t . (W0_i + s B_i A)) / n_i.
+struct DmRecompute {
+  const float* norm;
+  const void *gy, *x, *W0, *A, *B;
+  float s;
+  int64_t T, d_in, r;
+};
+
+// dm_i = sum_b dm_part[b, i] / m_i (fixed order); columns with m_i == 0 from `z`.
 hipError_t dm_finalize(const float* dm_part, int64_t blocks, const void* m, float* dm,
-                       int64_t d_out, int dtype, hipStream_t st);
+                       int64_t d_out, const DmRecompute& z, int dtype, hipStream_t st);
 
 // Launch bookkeeping for the optional per-kernel timing.
 struct LaunchTimer {

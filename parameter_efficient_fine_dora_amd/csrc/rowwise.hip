@@ -276,18 +276,58 @@ __global__ __launch_bounds__(256) void dora_compose_bwd(const void* gy, const vo
 
 // 64 columns per workgroup, the partial blocks split over 4 thread rows and
 // combined through LDS in a fixed order.
+//
+// dm_i = (sum_t gy[t,i] y[t,i]) / m_i rests on y / m = z / n, which says
+// nothing when m_i = 0 (column i of y is then 0 and carries no z).  Such a
+// column is recomputed from the definition, dm_i = sum_t gy[t,i] z[t,i] / n_i
+// with z[t,i] = x_t . V'_i and V'_i = W0_i + s B_i A: the workgroup's threads
+// share d_in, each forms its V'_ik and sum_t gy[t,i] x[t,k], and the products
+// meet in a fixed-order LDS reduction.  It costs T * (d_in + r) reads per zero
+// column and nothing when no m_i of the workgroup is zero.
 template <bool BF>
-__global__ __launch_bounds__(256) void dora_dm_finalize(const float* dm_part, int64_t blocks,
-                                                        const void* m, float* dm, int64_t d_out) {
+__global__ __launch_bounds__(256) void dora_dm_finalize(
+    const float* dm_part, int64_t blocks, const void* m, float* dm, int64_t d_out,
+    const float* norm, const void* gy, const void* x, const void* W0, const void* A,
+    const void* B, float s_lora, int64_t T, int64_t d_in, int64_t r) {
+  using V = Vec<BF>;
   __shared__ float red[4][64];
+  __shared__ float tree[256];
   const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int64_t i = (int64_t)blockIdx.x * 64 + c;
   float s = 0.f;
   if (i < d_out && q < blocks) s = sum_partials(dm_part + q * d_out + i, (blocks - q + 3) / 4, 4 * d_out);
   red[q][c] = s;
-  __syncthreads();
-  if (q == 0 && i < d_out)
-    dm[i] = ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) / Vec<BF>::scalar(m, i);
+  const bool zero_m = q == 0 && i < d_out && V::scalar(m, i) == 0.f;
+  if (!__syncthreads_or(zero_m)) {
+    if (q == 0 && i < d_out)
+      dm[i] = ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) / V::scalar(m, i);
+    return;
+  }
+  if (q == 0 && i < d_out && !zero_m)
+    dm[i] = ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) / V::scalar(m, i);
+  for (int cc = 0; cc < 64; ++cc) {
+    const int64_t col = (int64_t)blockIdx.x * 64 + cc;
+    if (col >= d_out) break;
+    if (V::scalar(m, col) != 0.f) continue;   // the same test in every thread
+    float acc = 0.f;
+    for (int64_t k = threadIdx.x; k < d_in; k += 256) {
+      float ba = 0.f;
+      for (int64_t j = 0; j < r; ++j) ba = fmaf(V::scalar(B, col * r + j), V::scalar(A, j * d_in + k), ba);
+      const float v = fmaf(s_lora, ba, V::scalar(W0, col * d_in + k));
+      float gx = 0.f;
+      for (int64_t t = 0; t < T; ++t)
+        gx = fmaf(V::scalar(gy, t * d_out + col), V::scalar(x, t * d_in + k), gx);
+      acc = fmaf(v, gx, acc);
+    }
+    tree[threadIdx.x] = acc;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+      if ((int)threadIdx.x < h) tree[threadIdx.x] += tree[threadIdx.x + h];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) dm[col] = tree[0] / fmaxf(norm[col], kNormEps);
+    __syncthreads();
+  }
 }
 
 // ---- undetached norm gradient (Appendix A.1 of the DoRA reading notes) -----------
@@ -552,15 +592,15 @@ hipError_t compose_bwd(const void* gy, const void* y, const void* m, const float
 }
 
 hipError_t dm_finalize(const float* dm_part, int64_t blocks, const void* m, float* dm,
-                       int64_t d_out, int dtype, hipStream_t st) {
+                       int64_t d_out, const DmRecompute& z, int dtype, hipStream_t st) {
   LaunchTimer t("dm_finalize", st);
   const dim3 grid((unsigned)cdiv(d_out, 64));
   if (dtype == kBF16)
     hipLaunchKernelGGL(dora_dm_finalize<true>, grid, dim3(256), 0, st, dm_part, blocks, m, dm,
-                       d_out);
+                       d_out, z.norm, z.gy, z.x, z.W0, z.A, z.B, z.s, z.T, z.d_in, z.r);
   else
     hipLaunchKernelGGL(dora_dm_finalize<false>, grid, dim3(256), 0, st, dm_part, blocks, m, dm,
-                       d_out);
+                       d_out, z.norm, z.gy, z.x, z.W0, z.A, z.B, z.s, z.T, z.d_in, z.r);
   return hipGetLastError();
 }
 

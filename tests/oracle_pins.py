@@ -210,6 +210,24 @@ def pin_fd_exact(orc):
         _close(an[k], fd[k], 1e-6, "exact FD " + k)
 
 
+def pin_fd_zero_magnitude(orc):
+    """Rows whose magnitude is zero (pruned, or trained to 0): y_i is then 0, but
+    L still depends on m_i, so dm_i is the finite difference, not 0 or NaN;
+    detached (n frozen) and exact."""
+    W0, A, B, m, x, gy = _layer(15, 4, 5, 2, 3)
+    m = m.copy()
+    m[[1, 3]] = 0.0
+    s = 1.3
+    n0 = orc.dora_norm(W0, A, B, s)
+    for frozen, exact in ((n0, False), (None, True)):
+        fd = _fd_grads(orc, dict(W0=W0, A=A, B=B, m=m, x=x), s, gy, frozen_norm=frozen)
+        an = orc.dora_backward(gy, x, W0, A, B, m, s, exact=exact)
+        for k in ("dx", "dA", "dB", "dm"):
+            assert np.all(np.isfinite(an[k])), k
+            _close(an[k], fd[k], 1e-6, f"m_i = 0 FD {k} (exact={exact})")
+        assert np.all(np.abs(an["dm"][[1, 3]]) > 1e-3), "a zero magnitude still has a gradient"
+
+
 def pin_eq8_closed_form(orc):
     W0, A, B, m, x, gy = _layer(12)
     s = 2.0
@@ -338,6 +356,6 @@ def pin_dvora_fd(orc):
 ALL_PINS = [
     pin_worked_rows, pin_bruteforce, pin_factored_identity, pin_b_zero, pin_g_one_is_lora,
     pin_scale_invariance, pin_s_zero_weightnorm, pin_token_permutation, pin_fd_detached,
-    pin_fd_exact, pin_eq8_closed_form, pin_b_zero_backward, pin_sampled_forms, pin_merged_weight,
+    pin_fd_exact, pin_fd_zero_magnitude, pin_eq8_closed_form, pin_b_zero_backward, pin_sampled_forms, pin_merged_weight,
     pin_dvora_reduces_to_dora, pin_dvora_vera_loops, pin_dvora_fd,
 ]

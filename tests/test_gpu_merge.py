@@ -103,3 +103,14 @@ def test_merge_fullsize_sampled(ops):
     L = synth.layer_f64({k: layer[k] for k in ("W0", "A", "B", "m")}, shape.dtype)
     ref = oracle.merged_weight(L["W0"][rows], L["A"], L["B"][rows], L["m"][rows], shape.s)
     check_out(got, ref, "merged rows")
+
+
+def test_merge_ragged_rows_on_the_eight_wave_tile(ops):
+    """d_out = 4104 on the merge's 256 x 256 tile: the last tile-row holds 8 rows of B."""
+    shape = LayerShape(4104, 4096, 16, 0, 2.0, "bf16")
+    print(f"merge ragged eight-wave tile {shape}", flush=True)
+    layer = synth.make_layer(shape, 35)
+    dev = layer_to_device(layer, shape.dtype)
+    got = download(ops.dora_merge(dev["W0"], dev["A"], dev["B"], dev["m"], shape.s))
+    L = synth.layer_f64(layer, shape.dtype)
+    check_out(got, oracle.merged_weight(L["W0"], L["A"], L["B"], L["m"], shape.s), "merged weight")

@@ -572,3 +572,51 @@ def test_exact_norm_gradient_fullsize_sampled(ops):
     check_out(got["dB"][rows], ref["dB"], "exact dB (sampled rows)")
     check_out(got["dA"][:, cols], ref["dA"], "exact dA (sampled columns)")
     check_out(got["dm"][rows], ref["dm"], "exact dm (sampled rows)")
+
+
+# ---- zero magnitudes: dm from the definition where y / m = z / n fails -------------
+
+ZERO_M = [
+    ("ragged_bf16", LayerShape(264, 520, 24, 37, 2.0, "bf16"), 31),
+    ("ragged_f32", LayerShape(264, 520, 24, 37, 2.0, "f32"), 32),
+    ("multitile_bf16", LayerShape(520, 1032, 136, 300, 2.0, "bf16"), 33),
+]
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 3], ids=["fused", "fused_exact", "separate",
+                                                     "separate_exact"])
+@pytest.mark.parametrize("name,shape,seed", ZERO_M, ids=[c[0] for c in ZERO_M])
+def test_zero_magnitude_rows(ops, name, shape, seed, flags):
+    """Rows with m_i = 0 (a pruned magnitude): y_i = 0 exactly, every gradient finite
+    and at the oracle's value, including dm_i (which the saved y cannot give)."""
+    say(f"zero magnitudes {name} flags={flags}")
+    layer = synth.make_layer(shape, seed, grad=True)
+    zero = np.array([0, 5, shape.d_out // 2, shape.d_out - 1])
+    layer["m"] = layer["m"].copy()
+    layer["m"][zero] = 0
+    got = run_layer(ops, shape, layer, flags=flags)
+    for k, v in got.items():
+        if v is not None:
+            assert np.all(np.isfinite(v)), k
+    assert not got["y"][:, zero].any(), "a zero magnitude gives a zero output column"
+    L = synth.layer_f64(layer, shape.dtype)
+    y_ref, n_ref = oracle.dora_forward(L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
+    check_norm(got["norm"], n_ref, "norm")
+    check_out(got["y"], y_ref, "y")
+    g = oracle.dora_backward(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s,
+                             exact=bool(flags & 1))
+    for k in ("dx", "dA", "dB", "dm"):
+        check_out(got[k], g[k], k)
+    check_out(got["dm"][zero], g["dm"][zero], "dm of the zero-magnitude rows")
+
+
+# ---- ragged token tile on the 256 x 256 (eight-wave) tile --------------------------
+
+def test_ragged_rows_on_the_eight_wave_tile(ops):
+    """T = 4100 on the 256 x 256 tile of the forward GEMM: its last tile-row holds 4
+    tokens, so the copies of x must range-check every row they load."""
+    shape = LayerShape(4096, 512, 16, 4100, 2.0, "bf16")
+    say(f"ragged eight-wave tile {shape}")
+    layer = synth.make_layer(shape, 34, grad=True)
+    got = run_layer(ops, shape, layer)
+    compare_full(shape, layer, got)
