@@ -8,18 +8,26 @@ r = 384, bf16).  Inputs are synthetic (seeded, see synth), resident in HBM
 before the timed region; every output and workspace buffer is allocated
 before it too.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
                     [--config NAME] [--cold] [--graph] [--separate-compose] [--no-peaks]
 
-Prints one JSON line.  ``value`` is microseconds per step (lower is better).
-``roofline`` covers the dominant kernel (largest share of the step), timed
-with HIP events on the library's launch stream over the timed steps;
-``kernels`` lists every kernel of the step the same way.  ``cpu_baseline``
-times the float64 oracle (dense W0 + sBA) on the host for one full step.
-``measured_peaks`` gives the achievable HBM copy rate and sustained MFMA
-rate measured in the same process; fractions of them sit beside the
-fractions of the published peaks.  ``--config`` times another synthetic
-layer's forward; ``--cold`` evicts the MALL before every step.
+Prints one JSON line.  ``value`` is microseconds per step (lower is better),
+from events between consecutive back-to-back steps (``step_spread`` summarises
+the same series).  ``roofline`` covers the dominant kernel (largest share of
+the step), timed with HIP events on the library's launch stream in a separate
+pass; ``kernels`` lists every kernel of the step the same way.  ``norm`` is the
+whole factored-norm chain (µs, algorithmic GB/s against 8 TB/s, fraction of
+its max(HBM, MFMA) bound); ``compose_fwd`` times the standalone one-pass
+compose kernel in the same process (the default path runs the compose as the
+forward GEMM's epilogue) and ``compose_bwd`` the backward's.  ``configs``
+gives the forward of the other synthetic layers (a tiny float32 layer, the
+2048 x 6144 crossover, the 8192 x 8192 headline and the 27648 x 5120 MLP).
+``cpu_baseline`` times the float64 oracle (dense W0 + sBA) on the host: norm,
+forward and backward separately, each the median of three after a warm-up.
+``measured_peaks`` gives the achievable HBM copy rate and sustained MFMA rate
+measured in the same process; fractions of them sit beside the fractions of
+the published peaks.  ``--config`` times another synthetic layer's forward;
+``--cold`` evicts the MALL before every step.
 """
 from __future__ import annotations
 
@@ -128,28 +136,66 @@ def kernel_table(timing, steps, work, traffic, peaks=None, flop_peak=None):
     return out
 
 
-def cpu_baseline(layer_np, shape, backward=True):
-    """The float64 oracle, as it stands, for one full step of the same layer."""
-    import numpy as np  # noqa: F401
-    import oracle
-    import synth
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 1) for i in threadpool_info()
-                      if i.get("user_api") == "blas")
+        return max((i.get("num_threads") or 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas")
     except Exception:  # noqa: BLE001
-        threads = os.cpu_count()
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(layer_np, shape, backward=True, reps=3):
+    """The float64 oracle, as it stands, on the host cores: its dense norm, forward
+    and (detached) backward of the same layer, each the median of ``reps`` runs
+    after one warm-up (input decoding excluded).  A float64 factored norm (the
+    oracle's base + cross + Gram terms, the GPU path's algorithm) is timed too."""
+    import numpy as np
+    import oracle
+    import synth
     L = synth.layer_f64(layer_np, shape.dtype)
-    t0 = time.perf_counter()
-    oracle.dora_forward(L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
-    if backward:
-        oracle.dora_backward(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s)
-    dt = time.perf_counter() - t0
-    what = "dense float64 forward + detached backward" if backward else "dense float64 forward"
-    return {"value": round(dt * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
+
+    def med(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)) * 1e6
+
+    def factored():
+        base, cross, gram = oracle.norm_terms(L["W0"], L["A"], L["B"], shape.s)
+        return np.sqrt(np.maximum(base + cross + gram, 0.0))
+
+    t_norm = med(lambda: oracle.dora_norm(L["W0"], L["A"], L["B"], shape.s))
+    t_fact = med(factored)
+    t_fwd = med(lambda: oracle.dora_forward(L["x"], L["W0"], L["A"], L["B"], L["m"], shape.s))
+    t_bwd = med(lambda: oracle.dora_backward(L["gy"], L["x"], L["W0"], L["A"], L["B"], L["m"],
+                                             shape.s)) if backward else 0.0
+    what = "forward + detached backward" if backward else "forward"
+    return {"value": round(t_fwd + t_bwd, 1), "unit": "us", "cores": _blas_threads(),
+            "kind": "oracle",
             "sample": f"one full step ({what}) of the same d_out={shape.d_out} d_in={shape.d_in} "
-                      f"r={shape.r} T={shape.tokens} layer, inputs decoded from the same "
-                      f"{shape.dtype} bits"}
+                      f"r={shape.r} T={shape.tokens} layer in float64 (dense W0 + sBA), inputs "
+                      f"decoded from the same {shape.dtype} bits; each part the median of "
+                      f"{reps} runs after one warm-up",
+            "norm_us": round(t_norm, 1), "forward_us": round(t_fwd, 1),
+            "backward_us": round(t_bwd, 1), "factored_norm_us": round(t_fact, 1),
+            "host_cpus": os.cpu_count(), "blas_threads": _blas_threads(),
+            "cpu_model": _cpu_model()}
 
 
 def measure_peaks(torch, ops, dev):
@@ -194,12 +240,119 @@ def measure_peaks(torch, ops, dev):
                    "v_mfma_f32_32x32x16_bf16 chains, 4096 workgroups of 4 waves"}
 
 
+# Kernels of the factored norm (dora_norm's chain inside dora_forward).
+NORM_LABELS = ("gram_AAt", "gram_finalize", "cross_gram_proj", "norm_finalize", "row_norm")
+# Forward-only workloads reported beside the headline step (synth.CONFIGS names).
+FORWARD_CONFIGS = ("tiny_f32", "crossover_bf16", "highrank_bf16", "widemlp_bf16")
+
+
+def norm_work(d_out, d_in, r, e=2):
+    """Algorithmic work of the whole factored norm: bytes = W0, A, B read once and
+    the norms written; flops = U = W0 A^T, G = A A^T and B G (2 per multiply-add)."""
+    nbytes = (d_out * d_in + r * d_in + d_out * r) * e + d_out * 4
+    flops = 2 * d_out * r * d_in + 2 * r * r * d_in + 2 * d_out * r * r
+    return nbytes, flops
+
+
+def norm_summary(timing, steps, d_out, d_in, r, e=2):
+    """The norm chain per step: µs, algorithmic GB/s against 8 TB/s, and the
+    fraction of its max(HBM, MFMA) bound."""
+    parts = {k: timing[k] for k in NORM_LABELS if k in timing}
+    if not parts or not steps:
+        return None
+    us = sum(tot for _, tot in parts.values()) / steps * 1e3
+    nbytes, flops = norm_work(d_out, d_in, r, e)
+    bound_us = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFS * 1e12)) * 1e6
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "launches_per_step": round(sum(c for c, _ in parts.values()) / steps, 2),
+            "kernels": sorted(parts), "bytes": nbytes, "gbps": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "flops": flops,
+            "bound_us": round(bound_us, 2), "frac_of_bound": round(bound_us / us, 4),
+            "bound": "max(bytes at 8 TB/s, flops at 2.5 PFLOP/s)"}
+
+
+def step_stats(per_ms):
+    import numpy as np
+    return {"median_us": round(float(np.median(per_ms)) * 1e3, 2),
+            "mean_us": round(float(np.mean(per_ms)) * 1e3, 2),
+            "min_us": round(float(np.min(per_ms)) * 1e3, 2),
+            "max_us": round(float(np.max(per_ms)) * 1e3, 2), "n": len(per_ms)}
+
+
+def timed_series(torch, run, steps):
+    """K back-to-back steps with an event between consecutive steps: the total
+    (first to last event) and every step's own duration come from one series."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for k in range(steps):
+        run()
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[k].elapsed_time(evs[k + 1]) for k in range(steps)]
+    return evs[0].elapsed_time(evs[-1]) / steps, per
+
+
+def _upload(torch, np, a, is_bf, dev):
+    a = np.ascontiguousarray(a)
+    if is_bf:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def forward_config(torch, np, ops, synth, name, dev, steps, warmup, tensors=None):
+    """Forward (factored norm + fused compose) of one synthetic layer: µs per
+    forward from events between consecutive back-to-back forwards, and the
+    per-kernel table of a separate pass."""
+    shape = synth.CONFIGS[name]
+    is_bf = shape.dtype == "bf16"
+    tdt = torch.bfloat16 if is_bf else torch.float32
+    e = 2 if is_bf else 4
+    d_out, d_in, r, T, s = shape.d_out, shape.d_in, shape.r, shape.tokens, shape.s
+    if tensors is None:
+        layer = synth.make_layer(shape, synth.CONFIG_SEED[name])
+        tensors = {k: _upload(torch, np, v, is_bf, dev) for k, v in layer.items()}
+    d = tensors
+    y = torch.empty(T, d_out, dtype=tdt, device=dev)
+    norm = torch.empty(d_out, dtype=torch.float32, device=dev)
+    xs = torch.empty(T, r, dtype=tdt, device=dev)
+    ws = torch.empty(max(1, ops.workspace_bytes(d_out, d_in, r, T, tdt, 1)), dtype=torch.uint8,
+                     device=dev)
+
+    def fwd():
+        ops.dora_forward(d["x"], d["W0"], d["A"], d["B"], d["m"], s, y=y, norm_out=norm,
+                         xs_out=xs, workspace=ws)
+
+    for _ in range(warmup):
+        fwd()
+    ms, per = timed_series(torch, fwd, steps)
+    ops.timing_enable(True)
+    for _ in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    ops.timing_enable(False)
+    timing = ops.timing_collect()
+    work = algorithmic_work(d_out, d_in, r, T, e)
+    flop_peak = BF16_PEAK_TFS if is_bf else FP32_PEAK_TFS
+    fwd_flops = 2 * T * d_out * (d_in + r) + 2 * T * r * d_in
+    nb, nf = norm_work(d_out, d_in, r, e)
+    return {"d_out": d_out, "d_in": d_in, "r": r, "tokens": T, "dtype": shape.dtype,
+            "fwd_us": round(ms * 1e3, 2), "per_forward": step_stats(per),
+            "launches_per_forward": round(sum(c for c, _ in timing.values()) / steps, 2),
+            "algorithmic_flops": fwd_flops + nf,
+            "tflops": round((fwd_flops + nf) / (ms * 1e-3) / 1e12, 2),
+            "norm": norm_summary(timing, steps, d_out, d_in, r, e),
+            "kernels": kernel_table(timing, steps, work, {}, None, flop_peak)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the forward-only timings of the other synthetic layers")
     ap.add_argument("--separate-compose", action="store_true",
                     help="run the standalone compose kernels instead of the GEMM-fused ones")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -244,14 +397,7 @@ def main():
     print(f"# generating inputs {args.config}: d_out={d_out} d_in={d_in} r={r} T={T}",
           file=sys.stderr, flush=True)
     layer = synth.make_layer(shape, synth.CONFIG_SEED[shape.name], grad=backward)
-
-    def up(a):
-        a = np.ascontiguousarray(a)
-        if is_bf:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    d = {k: up(v) for k, v in layer.items()}
+    d = {k: _upload(torch, np, v, is_bf, dev) for k, v in layer.items()}
     y = torch.empty(T, d_out, dtype=tdt, device=dev)
     norm = torch.empty(d_out, dtype=torch.float32, device=dev)
     xs = torch.empty(T, r, dtype=tdt, device=dev)
@@ -310,11 +456,11 @@ def main():
         torch.cuda.synchronize()
     print(f"# timing {args.steps} steps{' (cold)' if args.cold else ''}"
           f"{' (graph replays)' if args.graph else ''}", file=sys.stderr, flush=True)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if args.cold:
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
         per = []
         for _ in range(args.steps):
             evict.fill_(1)
@@ -325,27 +471,10 @@ def main():
             per.append(ev0.elapsed_time(ev1))
         ms_per_step = float(np.median(per))
     else:
-        ev0.record()
-        for _ in range(args.steps):
-            run()
-        ev1.record()
-        torch.cuda.synchronize()
-        ms_per_step = ev0.elapsed_time(ev1) / args.steps
+        ms_per_step, per = timed_series(torch, run, args.steps)
     wall = time.perf_counter() - t0
-    if not args.cold:
-        # the spread: the same number of steps again, each bracketed by its own
-        # events (outside the timed region; `value` stays the bracketed mean)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for a, b in evs:
-            a.record()
-            run()
-            b.record()
-        torch.cuda.synchronize()
-        per = [a.elapsed_time(b) for a, b in evs]
-    step_stats = {"median_us": round(float(np.median(per)) * 1e3, 2),
-                  "min_us": round(float(np.min(per)) * 1e3, 2),
-                  "max_us": round(float(np.max(per)) * 1e3, 2), "n": len(per)}
+    spread = step_stats(per)
+    spread["first_steps_us"] = [round(v * 1e3, 1) for v in per[:5]]
 
     # per-kernel times: the same steps again, each launch bracketed by HIP events
     print("# per-kernel timing", file=sys.stderr, flush=True)
@@ -360,6 +489,41 @@ def main():
     if args.serial:   # the timed steps' records, then the per-kernel pass's (same kernels)
         timing = {k: (v[0] / 2, v[1] / 2) for k, v in timing.items()}
 
+    # the standalone one-pass compose (the default path folds it into the forward
+    # GEMM's epilogue): a few separate-compose forwards in the same process
+    compose_fwd = None
+    if not args.cold:
+        sep = ops.FLAG_SEPARATE_COMPOSE
+        ws_sep = torch.empty(max(1, ops.workspace_bytes(d_out, d_in, r, T, tdt, 1, sep)),
+                             dtype=torch.uint8, device=dev)
+        y_sep = torch.empty_like(y)
+        for _ in range(3):
+            ops.dora_forward(d["x"], d["W0"], d["A"], d["B"], d["m"], s, y=y_sep, norm_out=norm,
+                             xs_out=xs, workspace=ws_sep, flags=sep)
+        torch.cuda.synchronize()
+        ops.timing_enable(True)
+        n_sep = max(5, min(args.steps, 20))
+        for _ in range(n_sep):
+            ops.dora_forward(d["x"], d["W0"], d["A"], d["B"], d["m"], s, y=y_sep, norm_out=norm,
+                             xs_out=xs, workspace=ws_sep, flags=sep)
+        torch.cuda.synchronize()
+        ops.timing_enable(False)
+        tsep = ops.timing_collect()
+        del ws_sep, y_sep
+        if "compose_fwd" in tsep:
+            cnt, tot = tsep["compose_fwd"]
+            us = tot / cnt * 1e3
+            nbytes = algorithmic_work(d_out, d_in, r, T, e)["compose_fwd"][1]
+            gbs = nbytes / (us * 1e-6) / 1e9
+            compose_fwd = {
+                "avg_us": round(us, 3), "bytes": nbytes, "gbps": round(gbs, 1),
+                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "how": "the standalone one-pass compose kernel (DORA_FLAG_SEPARATE_COMPOSE: "
+                       "read base and s*lora, write y), timed in the same process; the "
+                       "default path applies the same formula in the forward GEMM's "
+                       "epilogue, which adds only the m and n reads "
+                       f"({d_out * (e + 4)} bytes) to that GEMM"}
+
     peaks = None
     if not args.no_peaks:
         print("# achievable peaks (copy, MFMA probe)", file=sys.stderr, flush=True)
@@ -369,6 +533,8 @@ def main():
     headline = args.config == DEFAULT_CONFIG and not flags and not args.cold
     traffic = recorded_traffic() if headline else {}
     kernels = kernel_table(timing, args.steps, work, traffic, peaks, flop_peak)
+    if peaks and compose_fwd:
+        compose_fwd["frac_measured_hbm"] = round(compose_fwd["gbps"] / peaks["hbm_stream_GBs"], 4)
     # the dominant kernel among those with a work model (split-K reductions have none)
     dominant = max((k for k in timing if k in work), key=lambda k: timing[k][1])
     kind, amount = work[dominant]
@@ -378,7 +544,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": flop_peak,
                 "unit": "TFLOP/s", "frac": round(achieved / flop_peak, 4),
                 "traffic": traffic.get(dominant, {}).get("total_bytes"),
-                "kernel": dominant, "per_launch": f"{amount / 1e9:.1f} GFLOP"}
+                "kernel": dominant, "per_launch": f"{amount / 1e9:.1f} GFLOP",
+                "avg_us": round(avg_s * 1e6, 2)}
         if peaks and is_bf:
             roof["frac_of_measured"] = round(achieved / peaks["mfma_bf16_TFs"], 4)
     else:
@@ -386,13 +553,30 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic.get(dominant, {}).get("total_bytes"),
-                "kernel": dominant, "per_launch": f"{amount / 1e6:.1f} MB"}
+                "kernel": dominant, "per_launch": f"{amount / 1e6:.1f} MB",
+                "avg_us": round(avg_s * 1e6, 2)}
         if peaks:
             roof["frac_of_measured"] = round(achieved / peaks["hbm_stream_GBs"], 4)
 
+    configs = None
+    if backward and not args.no_configs and not args.cold and not args.graph and not flags:
+        configs = {}
+        for name in FORWARD_CONFIGS:
+            print(f"# forward of {name}", file=sys.stderr, flush=True)
+            reuse = None
+            if name == "highrank_bf16":   # the step's own layer: same shape and distributions
+                reuse = {k: d[k] for k in ("x", "W0", "A", "B", "m")}
+            configs[name] = forward_config(torch, np, ops, synth, name, dev,
+                                           max(10, min(args.steps, 50)), max(3, args.warmup),
+                                           reuse)
+            if reuse is not None:
+                configs[name]["inputs"] = "the backward layer's (same shape and distributions)"
+            torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
-        print("# cpu baseline (float64 oracle, one step)", file=sys.stderr, flush=True)
+        print("# cpu baseline (float64 oracle: norm, forward, backward)", file=sys.stderr,
+              flush=True)
         cpu = cpu_baseline(layer, shape, backward)
 
     if args.config == DEFAULT_CONFIG:
@@ -404,7 +588,7 @@ def main():
     rec = {
         "metric": metric, "value": round(ms_per_step * 1e3, 2), "unit": "us",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4), "step_spread": step_stats,
+        "ms_per_step": round(ms_per_step, 4), "step_spread": spread,
         "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": shape.dtype, "data": "synthetic",
         "config": {"workload": f"{workload}, {shape.dtype}", "name": args.config,
@@ -414,9 +598,13 @@ def main():
                    "launch": "HIP graph replay" if args.graph else "eager",
                    "parallelism": "dp1"},
         "roofline": roof,
+        "norm": norm_summary(timing, args.steps, d_out, d_in, r, e),
+        "compose_fwd": compose_fwd,
+        "compose_bwd": kernels.get("compose_bwd"),
         "cpu_baseline": cpu,
         "measured_peaks": peaks,
         "kernels": kernels,
+        "configs": configs,
         "kernel_source_hash": kernel_source_hash(),
         "wall_s_timed": round(wall, 3),
     }

@@ -73,3 +73,39 @@ def test_recorded_traffic_belongs_to_these_sources():
     d, r, T = 8192, 384, 4096
     floor = (d * d + r * d + T * (d + r) + T * d) * 2
     assert traffic["dx_gemm"]["total_bytes"] >= floor
+
+
+def test_norm_summary_arithmetic():
+    d, r = 8192, 384
+    nbytes, flops = bench.norm_work(d, d, r)
+    assert nbytes == (d * d + r * d + d * r) * 2 + d * 4
+    assert flops == 2 * d * r * d + 2 * r * r * d + 2 * d * r * r
+    # two kernels of the chain, 40 us per step in total over 2 steps
+    timing = {"gram_AAt": (2, 0.01), "cross_gram_proj": (2, 0.07), "dx_gemm": (2, 1.0)}
+    n = bench.norm_summary(timing, 2, d, d, r)
+    assert n["us"] == 40.0 and n["launches_per_step"] == 2.0
+    assert n["kernels"] == ["cross_gram_proj", "gram_AAt"]
+    assert abs(n["gbps"] - nbytes / 40e-6 / 1e9) < 0.1
+    bound = max(nbytes / 8e12, flops / 2.5e15) * 1e6
+    assert abs(n["bound_us"] - bound) < 0.01 and abs(n["frac_of_bound"] - bound / 40.0) < 1e-4
+    assert bench.norm_summary({"dx_gemm": (1, 1.0)}, 1, d, d, r) is None
+
+
+def test_step_stats_from_one_series():
+    per = [1.2, 1.1, 1.3, 1.15]
+    st = bench.step_stats(per)
+    assert st["n"] == 4 and st["min_us"] == 1100.0 and st["max_us"] == 1300.0
+    assert st["min_us"] <= st["mean_us"] <= st["max_us"]
+
+
+def test_cpu_baseline_protocol_on_a_tiny_layer():
+    import synth
+    shape = synth.LayerShape(16, 24, 8, 5, 2.0, "bf16")
+    layer = synth.make_layer(shape, 3, grad=True)
+    cb = bench.cpu_baseline(layer, shape, True, reps=3)
+    for k in ("value", "unit", "cores", "kind", "sample", "norm_us", "forward_us", "backward_us",
+              "factored_norm_us", "host_cpus", "blas_threads", "cpu_model"):
+        assert k in cb, k
+    assert cb["kind"] == "oracle" and cb["unit"] == "us"
+    assert abs(cb["value"] - (cb["forward_us"] + cb["backward_us"])) < 0.2
+    assert cb["cores"] >= 1 and cb["host_cpus"] >= 1
