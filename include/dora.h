@@ -130,6 +130,30 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
                           void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
+ * dora_forward for callers that cannot allocate device memory (code under HIP
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and validation as dora_forward, without ws / ws_bytes:
+ * the workspace is a static device array of DORA_NOALLOC_SCRATCH_BYTES inside
+ * the library, one copy on every GPU the library runs on, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no stream or event
+ * creation): every launch goes on hip_stream, without the side stream.
+ *   Limit     shapes whose dora_workspace_bytes(shape, DORA_OP_FORWARD) exceeds
+ *             DORA_NOALLOC_SCRATCH_BYTES return DORA_ERR_WORKSPACE (nothing is
+ *             enqueued); every configuration up to d_out 27648, d_in 8192,
+ *             r 384 and 8192 tokens fits.
+ *   Sharing   all calls on one GPU use that GPU's one array, which keeps the last
+ *             call's contents (nothing in it needs to start at zero).  Calls that
+ *             overlap on one GPU (concurrent streams, or host threads) race on
+ *             it: order them on one stream, or use dora_forward.
+ *   Errors    as dora_forward; DORA_ERR_HIP also if the array's device address
+ *             cannot be looked up.
+ */
+#define DORA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+DORA_API int dora_forward_noalloc(const dora_shape* shape, const void* x, const void* W0,
+                                  const void* A, const void* B, const void* m, void* y,
+                                  float* norm_out, void* xs_out, void* hip_stream);
+
+/*
  * Backward of dora_forward for L with dL/dy = grad_y.  By default the norm is
  * detached, i.e. held constant (DoRA reading notes Sec. 3.4, the default
  * implementation there):

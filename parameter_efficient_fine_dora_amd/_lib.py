@@ -15,6 +15,7 @@ OP_NORM, OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_VERA_GRADS = 0, 1, 2, 3, 4
 ERR = {0: "DORA_OK", -1: "DORA_ERR_NULL", -2: "DORA_ERR_SHAPE", -3: "DORA_ERR_DTYPE",
        -4: "DORA_ERR_ALIGN", -5: "DORA_ERR_WORKSPACE", -6: "DORA_ERR_HIP", -7: "DORA_ERR_FLAGS"}
 ERR_CODE = {v: k for k, v in ERR.items()}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # DORA_NOALLOC_SCRATCH_BYTES
 
 
 class DoraShape(ctypes.Structure):
@@ -38,6 +39,8 @@ _SIGS = {
     "dora_norm": (_i, [ctypes.POINTER(DoraShape), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dora_forward": (_i, [ctypes.POINTER(DoraShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _sz, _vp]),
+    "dora_forward_noalloc": (_i, [ctypes.POINTER(DoraShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp]),
     "dora_backward": (_i, [ctypes.POINTER(DoraShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dora_merge": (_i, [ctypes.POINTER(DoraShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "../../include/dora.h"
+#include "entry.h"
 #include "kernels.h"
 
 namespace dora {
@@ -428,6 +429,16 @@ DORA_API int dora_norm(const dora_shape* shape, const void* W0, const void* A, c
 DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0, const void* A,
                           const void* B, const void* m, void* y, float* norm_out, void* xs_out,
                           void* ws, size_t ws_bytes, void* hip_stream) {
+  return forward_impl(shape, x, W0, A, B, m, y, norm_out, xs_out, ws, ws_bytes, hip_stream, true);
+}
+
+}  // extern "C"
+
+namespace dora {
+
+int forward_impl(const dora_shape* shape, const void* x, const void* W0, const void* A,
+                 const void* B, const void* m, void* y, float* norm_out, void* xs_out, void* ws,
+                 size_t ws_bytes, void* hip_stream, bool allow_side_stream) {
   DORA_CHECK(check_common(shape, DORA_OP_FORWARD, ws, ws_bytes));
   const dora_shape& s = *shape;
   const bool noT = s.tokens == 0;
@@ -447,7 +458,7 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
   // on the norm (and uses other workspace regions), so it runs on a side
   // stream beside the norm's chain and joins before the forward GEMM.
   void* xs = xs_out ? xs_out : at(ws, L.xs);
-  SideStream* side = (!noT && s.r > 0) ? side_stream() : nullptr;
+  SideStream* side = (allow_side_stream && !noT && s.r > 0) ? side_stream() : nullptr;
   auto down_proj = [&](hipStream_t on) -> int {
     GemmProblem d;
     d.M = s.tokens;
@@ -512,6 +523,10 @@ DORA_API int dora_forward(const dora_shape* shape, const void* x, const void* W0
   HIP_TRY(gemm(f, dt, st, "fused_fwd_gemm"));
   return DORA_OK;
 }
+
+}  // namespace dora
+
+extern "C" {
 
 DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const void* x,
                            const void* W0, const void* A, const void* B, const void* m,

@@ -116,6 +116,35 @@ def dora_forward(x, W0, A, B, m, s, *, y=None, norm_out=None, xs_out=None, keep_
     return y, norm_out, xs_out
 
 
+def dora_forward_noalloc(x, W0, A, B, m, s, *, y=None, norm_out=None, xs_out=None, flags=0):
+    """dora_forward on the library's static workspace (no workspace argument; the
+    library allocates nothing).  Outputs not given are allocated here by torch,
+    before the call.  Returns (y, norm, xs or None)."""
+    dev = W0.device
+    dt = W0.dtype
+    d_out, d_in = W0.shape
+    r = A.shape[0]
+    T = x.shape[0]
+    _need(W0, "W0", dt)
+    _need(x, "x", dt, (T, d_in), dev)
+    _need(A, "A", dt, (r, d_in), dev)
+    _need(B, "B", dt, (d_out, r), dev)
+    _need(m, "m", dt, (d_out,), dev)
+    sh = _lib.shape(d_out, d_in, r, T, _layer_dtype(W0), s, flags)
+    if y is None:
+        y = torch.empty(T, d_out, dtype=dt, device=dev)
+    if norm_out is None:
+        norm_out = torch.empty(d_out, dtype=torch.float32, device=dev)
+    _need(y, "y", dt, (T, d_out), dev)
+    _need(norm_out, "norm_out", torch.float32, (d_out,), dev)
+    if xs_out is not None:
+        _need(xs_out, "xs_out", dt, (T, r), dev)
+    _check(_lib.lib().dora_forward_noalloc(ctypes.byref(sh), _ptr(x), _ptr(W0), _ptr(A), _ptr(B),
+                                           _ptr(m), _ptr(y), _ptr(norm_out), _ptr(xs_out),
+                                           _stream(dev)), "dora_forward_noalloc")
+    return y, norm_out, xs_out
+
+
 def dora_backward(grad_y, x, W0, A, B, m, norm, xs, y, s, *, need=("x", "A", "B", "m"),
                   grad_x=None, grad_A=None, grad_B=None, grad_m=None, workspace=None, flags=0):
     """DoRA linear backward with the norm detached.
