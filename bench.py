@@ -51,7 +51,8 @@ DEFAULT_CONFIG = "highrank_bwd_bf16"
 
 KERNEL_SOURCES = ["include/dora.h"] + [
     f"parameter_efficient_fine_dora_amd/csrc/{f}"
-    for f in ("api.hip", "gemm.hip", "rowwise.hip", "common.h", "kernels.h")]
+    for f in ("api.hip", "gemm.hip", "gram.hip", "rowwise.hip", "noalloc.hip", "common.h",
+              "kernels.h", "entry.h")]
 WORKLOAD_TAG = "highrank_d8192_r384_t4096"
 
 
@@ -87,9 +88,6 @@ def algorithmic_work(d_out, d_in, r, T, e=2):
     return {
         "gram_AAt": ("flop", 2 * r * r * d_in),
         "cross_gram_proj": ("flop", 2 * d_out * r * d_in + 2 * d_out * r * r),
-        # the projection hands over per-row partials; their count is a tiling
-        # detail, so the finalize counts one float in and one out per row
-        "norm_finalize": ("byte", d_out * 4 + d_out * 4),
         "row_norm": ("byte", d_out * d_in * e + d_out * r * e + d_out * r * 4 + d_out * 4),
         "down_proj_xs": ("flop", 2 * T * r * d_in),
         "fused_fwd_gemm": ("flop", 2 * T * d_out * (d_in + r)),

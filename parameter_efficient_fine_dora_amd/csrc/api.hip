@@ -83,9 +83,16 @@ int gram_splits(const dora_shape& s) {
 // (||W0_i||^2 from its pass over W0, B_i . P_i from its accumulators); P
 // itself is never stored.
 bool fused_norm(const dora_shape& s) { return s.dtype == kBF16 && s.r > 0; }
-int p_cfg(const dora_shape& s) { return plan_gemm(s.d_out, s.r, p_depth(s), s.dtype).cfg; }
-
-int p_splits(const dora_shape& s) {
+// bf16 projections use their own planner (one column tile where the rank fits);
+// float32 ones (and the undetached gradient's Q, which stores P) the generic one.
+GemmPlan p_plan(const dora_shape& s) {
+  if (fused_norm(s)) return plan_norm_projection(s.d_out, s.r, p_depth(s), std::max(s.d_in, s.r));
+  return plan_gemm(s.d_out, s.r, p_depth(s), s.dtype);
+}
+int p_cfg(const dora_shape& s) { return p_plan(s).cfg; }
+int p_splits(const dora_shape& s) { return s.r > 0 ? p_plan(s).split : 1; }
+// the stored-P projection of the undetached gradient (generic planner)
+int q_splits(const dora_shape& s) {
   return s.r > 0 ? plan_gemm(s.d_out, s.r, p_depth(s), s.dtype).split : 1;
 }
 
@@ -124,9 +131,13 @@ Layout layout(const dora_shape& s, int op) {
     scratch = std::max(scratch, gemm_scratch_bytes(M, N, K, dt, akc, bkc));
   };
   if (op == DORA_OP_NORM || op == DORA_OP_FORWARD || op == DORA_OP_MERGE) {
-    L.splits = gram_splits(s);
     L.psplits = p_splits(s);
-    L.gpart = take((size_t)L.splits * r * r * 4);
+    if (fused_norm(s)) {   // bf16: the triangular Gram kernel's partial sums
+      L.gpart = take(gram_bf16_plan(s.r, s.d_in).part_bytes);
+    } else {
+      L.splits = gram_splits(s);
+      L.gpart = take((size_t)L.splits * r * r * 4);
+    }
     L.ghi = take(r * r * (s.dtype == kBF16 ? 2 : 4));
     L.glo = take(s.dtype == kBF16 ? r * r * 2 : 0);
     if (fused_norm(s)) {
@@ -175,7 +186,7 @@ Layout layout(const dora_shape& s, int op) {
       L.egpart = take((size_t)L.splits * r * r * 4);
       L.eghi = take(r * r * (s.dtype == kBF16 ? 2 : 4));
       L.eglo = take(s.dtype == kBF16 ? r * r * 2 : 0);
-      L.qsplits = p_splits(s);
+      L.qsplits = q_splits(s);
       L.q = take((size_t)L.qsplits * s.d_out * r * 4);
       L.hsplits = plan_gemm(s.r, s.r, s.d_out, dt, false, false).split;
       L.hpart = take((size_t)L.hsplits * r * r * 4);
@@ -333,18 +344,24 @@ int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, 
   float* gpart = reinterpret_cast<float*>(at(ws, L.gpart));
   void* ghi = at(ws, L.ghi);
   void* glo = at(ws, L.glo);
-  GemmProblem g;
-  g.M = g.N = s.r;
-  g.nseg = 1;
-  g.seg[0] = {A, A, s.d_in, s.d_in, s.d_in};
-  g.c = gpart;
-  g.ldc = s.r;
-  g.out_f32 = true;
-  g.split = L.splits;
-  g.split_stride = s.r * s.r;
-  g.cfg = plan_gemm(s.r, s.r, s.d_in, dt).cfg;
-  HIP_TRY(gemm(g, dt, st, "gram_AAt"));
-  HIP_TRY(gram_finalize(gpart, L.splits, s.r, 0.5f * s.s, dt, ghi, glo, st, "gram_finalize"));
+  if (fused_norm(s)) {
+    const GramPlan gp = gram_bf16_plan(s.r, s.d_in);
+    HIP_TRY(gram_bf16(A, s.r, s.d_in, gp, gpart, st));
+    HIP_TRY(gram_bf16_finish(gpart, gp, s.r, 0.5f * s.s, ghi, glo, nullptr, 0, st));
+  } else {
+    GemmProblem g;
+    g.M = g.N = s.r;
+    g.nseg = 1;
+    g.seg[0] = {A, A, s.d_in, s.d_in, s.d_in};
+    g.c = gpart;
+    g.ldc = s.r;
+    g.out_f32 = true;
+    g.split = L.splits;
+    g.split_stride = s.r * s.r;
+    g.cfg = plan_gemm(s.r, s.r, s.d_in, dt).cfg;
+    HIP_TRY(gemm(g, dt, st, "gram_AAt"));
+    HIP_TRY(gram_finalize(gpart, L.splits, s.r, 0.5f * s.s, dt, ghi, glo, st, "gram_finalize"));
+  }
 
   GemmProblem p;
   p.M = s.d_out;

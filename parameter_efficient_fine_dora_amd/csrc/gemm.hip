@@ -63,8 +63,9 @@ struct KArgs {
   const float* norm;
   const void* add;
   int64_t ld_add;
-  float* rowsq;          // kEpiNorm: [gridDim.y][M] sums of squares of opA over segment 0
-  float* rowdot;         // kEpiNorm: [gridDim.y][tiles_n][WN][M] row dots of alpha*C with `add`
+  float* rowsq;          // kEpiNorm: [nsplit][M] sums of squares of opA over segment 0
+  float* rowdot;         // kEpiNorm: [nsplit][tiles_n][WN][M] row dots of alpha*C with `add`
+  int nsplit;            // K splits (the bf16 kernels' grid is tiles x nsplit, 1-D)
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
@@ -105,7 +106,9 @@ template <int R, int NW>
 struct CopyKC {
   static constexpr int kInstr = R / 8 / NW;   // 16-byte copies per lane and stage
   static_assert(R % (8 * NW) == 0, "rows must split evenly over the waves");
-  static_assert(R <= 256, "R rows of a stride below 2^22 elements must span < 2^31 bytes");
+  // Per-lane offsets reach (R - 1) * ld * 2 + 112; the planner keeps R * ld * 2
+  // below 2^31 (always true for R <= 256, since every stride is below 2^22).
+  static_assert(R <= 384, "tile rows");
   // Instruction i of a wave fills rows (wave + i*NW)*8 .. +8.  With NW a
   // multiple of 8 every instruction sees the same swizzle, so one per-lane
   // offset serves them all: on a full tile the row step goes into the scalar
@@ -257,28 +260,34 @@ struct CopyMC {
 
 // M/N-contiguous operand copied straight into LDS (buffer_load ... lds) in
 // its own k-major layout: a stage is 64 k-rows of R elements (2R bytes), the
-// 16-byte chunks of k-row k XOR-swizzled by 4*(k % 4).  One wave instruction
-// fills 1 KiB = kKPI k-rows; lane l takes k-row l / kLPR and physical chunk
-// l % kLPR.  The MFMA fragments are then read with the transposing LDS read
-// (ds_read_b64_tr_b16, see tr_frag); the swizzle spreads the four k-rows one
-// 16-lane group of that read touches over distinct banks.  Columns past the
-// operand carry kOob from the start; k-rows past K are masked on a segment's
-// last step only.
+// 16-byte chunks of k-row k XOR-swizzled by 4*(k % 4).  The stage's chunks are
+// numbered row by row, c = k-row * kLPR + chunk, and sit at byte 16 c of the
+// stage, so one wave instruction fills the 1 KiB of chunks 64 j .. 64 j + 63
+// (lane l takes chunk 64 j + l); R need not be a power of two (a 384-wide
+// k-row is 48 chunks).  The MFMA fragments are then read with the transposing
+// LDS read (ds_read_b64_tr_b16, see tr_frag); the swizzle spreads the four
+// k-rows one 16-lane group of that read touches over distinct banks (an XOR
+// by at most 12 keeps a chunk inside its 16-chunk group, so inside the row).
+// Columns past the operand carry kOob from the start; k-rows past K are
+// masked on a segment's last step only.
 template <int R, int NW>
 struct CopyNC {
   static constexpr int kRowB = R * 2;        // bytes of one k-row
-  static constexpr int kLPR = kRowB / 16;    // lanes (16-byte chunks) per k-row
-  static constexpr int kKPI = 64 / kLPR;     // k-rows per wave instruction
-  static constexpr int kInstr = kBK / kKPI / NW;
-  static_assert(kLPR >= 16 && kBK % (kKPI * NW) == 0, "k-rows must split evenly over the waves");
+  static constexpr int kLPR = kRowB / 16;    // 16-byte chunks per k-row
+  static constexpr int kInstr = kBK * kLPR / 64 / NW;
+  static_assert(kLPR >= 16 && kLPR % 16 == 0 && (kBK * kLPR) % (64 * NW) == 0,
+                "k-rows must split evenly over the waves");
   Rsrc rs;
   const uint16_t* base;    // column row0, k = 0
   int64_t ld;
   int kt_base;             // step the descriptor starts at
   int kt_span;             // steps one descriptor covers with a 31-bit scalar offset
   uint32_t off[kInstr];    // k-row * ld * 2 + logical chunk * 16, or kOob
+  __device__ __forceinline__ static int chunk_of(int i, int wave, int lane) {
+    return (wave + i * NW) * 64 + lane;
+  }
   __device__ __forceinline__ static int krow_of(int i, int wave, int lane) {
-    return (wave + i * NW) * kKPI + lane / kLPR;
+    return chunk_of(i, wave, lane) / kLPR;
   }
   __device__ __forceinline__ void prepare(const uint16_t* p, int64_t ldv, int row0, int nrows,
                                           int K, int wave, int lane, int) {
@@ -289,8 +298,9 @@ struct CopyNC {
     rs = make_rsrc(base, (int64_t)K * ldv * 2);
 #pragma unroll
     for (int i = 0; i < kInstr; ++i) {
-      const int kr = krow_of(i, wave, lane);
-      const int lc = (lane % kLPR) ^ (4 * (kr & 3));
+      const int c = chunk_of(i, wave, lane);
+      const int kr = c / kLPR;
+      const int lc = (c - kr * kLPR) ^ (4 * (kr & 3));
       off[i] = row0 + lc * 8 < nrows ? (uint32_t)kr * (uint32_t)(ldv * 2) + (uint32_t)lc * 16u
                                      : kOob;
     }
@@ -396,6 +406,32 @@ __device__ __forceinline__ int2 tile_coords(int tiles_m, int tiles_n) {
   return make_int2(first + rem % gsz, rem / gsz);
 }
 
+// bf16 kernels: a 1-D grid of tiles x K splits.  After the same XCD remap the
+// index is split-major, so an XCD's contiguous run covers one K split (or a
+// few): the operand slice a split shares between its tiles (e.g. A's K range
+// in x A^T) is then read by one XCD's L2 instead of by all of them.  Returns
+// tile_m, tile_n and the split index.
+__device__ __forceinline__ int3 tile_split_coords(int tiles_m, int tiles_n, int nsplit) {
+  int L = blockIdx.x;
+  const int nwg = gridDim.x;
+  const int tiles = tiles_m * tiles_n;
+  int group = 8;
+  if ((nwg & 7) == 0) {
+    L = (L & 7) * (nwg >> 3) + (L >> 3);
+    const int run = nwg >> 3;
+    if (tiles_n * tiles_n <= run && run % tiles_n == 0) group = run / tiles_n;
+  }
+  const int split = L / tiles;
+  L -= split * tiles;
+  const int per_group = group * tiles_n;
+  const int g = L / per_group;
+  const int first = g * group;
+  const int gsz = min(tiles_m - first, group);
+  const int rem = L - g * per_group;
+  (void)nsplit;
+  return make_int3(first + rem % gsz, rem / gsz, split);
+}
+
 template <bool OUT_F32>
 __device__ __forceinline__ void store4(void* cbase, int64_t ldc, int m, int n, float v0, float v1,
                                        float v2, float v3) {
@@ -446,7 +482,7 @@ __device__ __forceinline__ void wait_vmem_le() {
 // go straight out.
 template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
 __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
-                                              uint16_t* stg, void* c, int64_t ldc,
+                                              uint16_t* stg, int split, void* c, int64_t ldc,
                                               int64_t split_stride, float alpha, const void* mag,
                                               const float* nrm, const void* add, int64_t ld_add,
                                               int M, int N, int m0, int n0, int wave, int wm,
@@ -456,8 +492,8 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / W
   constexpr int kStageLd = TN + 8;
   // Epilogue.  acc[i][j][v]: m = m0 + wm*TM + i*32 + lane%32,
   //                          n = n0 + wn*TN + j*32 + (v/4)*8 + (lane/32)*4 + v%4.
-  void* cbase = OUT_F32 ? (void*)(reinterpret_cast<float*>(c) + blockIdx.y * split_stride)
-                        : (void*)(reinterpret_cast<uint16_t*>(c) + blockIdx.y * split_stride);
+  void* cbase = OUT_F32 ? (void*)(reinterpret_cast<float*>(c) + split * split_stride)
+                        : (void*)(reinterpret_cast<uint16_t*>(c) + split * split_stride);
   if constexpr (!OUT_F32) {
     // The K loop ended on a barrier, so every stage is free.  A wave's LDS
     // accesses complete in order, so block i + 1 may overwrite what block i
@@ -580,10 +616,11 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
   const int M = p.M, N = p.N;
-  const int2 tc = tile_coords(p.tiles_m, p.tiles_n);
+  const int3 tc = tile_split_coords(p.tiles_m, p.tiles_n, p.nsplit);
   const int m0 = __builtin_amdgcn_readfirstlane(tc.x * BM);
   const int n0 = __builtin_amdgcn_readfirstlane(tc.y * BN);
-  const int kt_lo = blockIdx.y * p.kt_per_split;
+  const int split = __builtin_amdgcn_readfirstlane(tc.z);
+  const int kt_lo = split * p.kt_per_split;
   const int kt_hi = min(kt_lo + p.kt_per_split, p.kt_total);
   const int kt_end0 = p.kt_end[0], kt_end1 = p.kt_end[1], kt_end2 = p.kt_end[2];
   const uint16_t *a0 = p.a[0], *a1 = p.a[1], *a2 = p.a[2];
@@ -601,10 +638,13 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   constexpr bool kRowSq = EPI == kEpiNorm;
-  const bool sq_wave = kRowSq && wn == 0 && tc.y == 0;
+  // kEpiNorm: the waves of the first wave column of the first column tile sum
+  // the squares of the opA fragments they read (VALU work beside the MFMAs) and
+  // keep the sums of segment 0.
   float sq[2][MB];   // kEpiNorm: per-lane partial sums of squares of the lane's opA rows
+  float sq0[MB];     // the same at the end of segment 0
 #pragma unroll
-  for (int i = 0; i < MB; ++i) sq[0][i] = sq[1][i] = 0.f;
+  for (int i = 0; i < MB; ++i) sq[0][i] = sq[1][i] = sq0[i] = 0.f;
 
   // Fragment read bases: the swizzle of row wm*TM + i*32 + lane%32 depends on i
   // only through its parity, and the chunk of step kk only through an XOR.
@@ -696,12 +736,20 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
                                                       acc[i][j], 0, 0, 0);                 \
       __builtin_amdgcn_sched_barrier(0);                                                   \
       if (SQ) {                                                                            \
-        _Pragma("unroll") for (int i = 0; i < MB; ++i)                                     \
-            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                \
-          /* the pair is built from elements: a bit_cast of a vector element */            \
-          /* (w[q]) compiles to a read of element 0 with this clang          */            \
-          const bf16x2 h_ = {af[kk & 1][i][2 * q], af[kk & 1][i][2 * q + 1]};              \
-          sq[kk & 1][i] = __builtin_amdgcn_fdot2_f32_bf16(h_, h_, sq[kk & 1][i], false);   \
+        /* elements 2q, 2q+1 share one 32-bit register: a shuffle of that pair */          \
+        /* selects it without repacking                                        */          \
+        _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                   \
+          const bf16x8 f_ = af[kk & 1][i];                                                 \
+          const bf16x2 h0_ = __builtin_shufflevector(f_, f_, 0, 1);                        \
+          const bf16x2 h1_ = __builtin_shufflevector(f_, f_, 2, 3);                        \
+          const bf16x2 h2_ = __builtin_shufflevector(f_, f_, 4, 5);                        \
+          const bf16x2 h3_ = __builtin_shufflevector(f_, f_, 6, 7);                        \
+          float t_ = sq[kk & 1][i];                                                        \
+          t_ = __builtin_amdgcn_fdot2_f32_bf16(h0_, h0_, t_, false);                       \
+          t_ = __builtin_amdgcn_fdot2_f32_bf16(h1_, h1_, t_, false);                       \
+          t_ = __builtin_amdgcn_fdot2_f32_bf16(h2_, h2_, t_, false);                       \
+          t_ = __builtin_amdgcn_fdot2_f32_bf16(h3_, h3_, t_, false);                       \
+          sq[kk & 1][i] = t_;                                                              \
         }                                                                                  \
       }                                                                                    \
     }                                                                                      \
@@ -744,11 +792,16 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
     wait_vmem();                                                                           \
     barrier_nofence();                                                                     \
   }
-    // Row sums of squares ride on the segment-0 fragments that the first
-    // column of waves of the first column of tiles already holds (a
-    // wave-uniform flag; a loop copy per case would double the live registers).
-    const bool sq_now = kRowSq && seg == 0 && sq_wave;
-    DORA_STAGES(sq_now)
+    // Row sums of squares ride on the fragments that the first wave column of
+    // the first column tile already holds (a flag fixed for the whole kernel,
+    // so the compiler keeps the other waves' loop free of it); the sums of
+    // segment 0 are kept when it ends.
+    const bool sq_w = kRowSq && wn == 0 && tc.y == 0;
+    DORA_STAGES(sq_w)
+    if (kRowSq && seg == 0) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) sq0[i] = sq[0][i] + sq[1][i];
+    }
   }
 #undef DORA_STAGES
 #undef DORA_FETCH
@@ -761,15 +814,16 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   if constexpr (kRowSq) {
     // Lane l and lane l + 32 hold the two halves of every 16-deep step of
     // one row; each split writes its partial (zero if it saw no segment-0 step).
-    if (sq_wave) {
+    if (wn == 0 && tc.y == 0) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
-        float v = sq[0][i] + sq[1][i];
+        float v = sq0[i];
         v += __shfl_xor(v, 32);
         const int m = m0 + wm * TM + i * 32 + lane;
-        if (lane < 32 && m < M) p.rowsq[(int64_t)blockIdx.y * M + m] = v;
+        if (lane < 32 && m < M) p.rowsq[(int64_t)split * M + m] = v;
       }
     }
+    const int64_t slot = ((int64_t)split * p.tiles_n + tc.y) * WN + wn;
     // C itself is not stored: each lane dots its accumulators with the rows
     // of `add` at the same (m, n) (in-lane over j, g, e, then the two lanes
     // that share a row), one partial per split, column tile and wave column.
@@ -795,7 +849,6 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
         }
       }
     }
-    const int64_t slot = ((int64_t)blockIdx.y * p.tiles_n + tc.y) * WN + wn;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       float v = dot[i];
@@ -811,7 +864,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
               : ((wave & 3) == 0 ? smem : (wave & 3) == 1 ? sA1 : (wave & 3) == 2 ? sB0 : sB1) +
                     (wave >> 2) * kStgBytes;
   uint16_t* const stg = reinterpret_cast<uint16_t*>(stg_obj);
-  gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, stg, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
+  gemm_epilogue<BM, BN, WM, WN, EPI, OUT_F32>(acc, stg, split, p.c, p.ldc, p.split_stride, p.alpha, p.mag,
                                                 p.norm, p.add, p.ld_add, M, N, m0, n0, wave, wm,
                                                 wn, lane);
 }
@@ -947,6 +1000,8 @@ constexpr Cfg kCfgs[] = {
     {128, 256, 2, 2},   // 3: 4 waves, 64x128 per wave
     {64, 64, 2, 2},     // 4: 4 waves, 32x32 per wave
     {256, 128, 4, 2},   // 5: 8 waves, 64x64 per wave
+    {128, 384, 2, 4},   // 6: 8 waves, 64x96 per wave (N = rank 384 in one tile)
+    {384, 128, 4, 2},   // 7: 8 waves, 96x64 per wave (M = rank 384 in one tile)
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -1009,6 +1064,8 @@ hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool
     case 3: return launch_layout<128, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 4: return launch_layout<64, 64, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 5: return launch_layout<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 6: return launch_layout<128, 384, 2, 4>(akc, bkc, a, epi, out_f32, grid, st);
+    case 7: return launch_layout<384, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1073,7 +1130,8 @@ hipError_t run(int cfg, int split, const GemmProblem& p, KArgs& a, int kt, hipSt
   a.tiles_n = (int)cdiv64(p.N, c.bn);
   a.kt_per_split = split > 1 ? (kt + split - 1) / split : (kt > 0 ? kt : 1);
   if (a.kt_per_split < 1) a.kt_per_split = 1;
-  const dim3 grid(a.tiles_m * a.tiles_n, split);
+  a.nsplit = split;
+  const dim3 grid(a.tiles_m * a.tiles_n * split);
   return launch_cfg(cfg, p.a_kcontig, p.b_kcontig, a, p.epi, out_f32, grid, st);
 }
 
@@ -1105,6 +1163,28 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bk
   split = std::min<int64_t>(split, std::max<int64_t>(1, ktiles / 8));
   split = std::max<int64_t>(1, std::min<int64_t>(split, 16));
   return {cfg, (int)split};
+}
+
+GemmPlan plan_norm_projection(int64_t M, int64_t N, int64_t K, int64_t ld_max) {
+  if (M <= 0 || N <= 0) return {-1, 1};
+  // A rank of 257..384 fits one 128 x 384 tile: opA (W0) then crosses L2 once
+  // per K split, and four splits of a d_out = 8192 layer make one workgroup
+  // per CU (measured 62-65 us against 78-81 us for 128 x 128 tiles there).
+  // Only while 384 rows of the widest operand span < 2^31 bytes.  Other ranks
+  // keep the generic plan (128 x 128 tiles, measured fastest at r = 256).
+  if (N > 256 && N <= 384 && ld_max * 2 * 384 < (int64_t(1) << 31)) {
+    const int64_t tiles = cdiv64(M, kCfgs[6].bm);
+    int64_t split = (256 + tiles / 2) / tiles;
+    split = std::min<int64_t>(split, std::max<int64_t>(1, cdiv64(K, kBK) / 8));
+    split = std::max<int64_t>(1, std::min<int64_t>(split, 16));
+    return {6, (int)split};
+  }
+  return plan_gemm(M, N, K, kBF16);
+}
+
+int64_t gemm_tile_rows(int cfg, int64_t M) {
+  if (cfg < 0 || cfg >= kNumCfgs) return 0;
+  return cdiv64(M, kCfgs[cfg].bm);
 }
 
 int64_t gemm_col_slots(int cfg, int64_t N) {

@@ -21,9 +21,10 @@ enum Epilogue : int {
   kEpiStore = 0,     // C = alpha * acc
   kEpiCompose = 1,   // C = z + (g - 1) z with z = alpha * acc, g_n = m_n / max(norm_n, eps)
   kEpiMerge = 2,     // C = g_m (add + alpha * acc) with g_m = m_m / max(norm_m, eps) per ROW
-  kEpiNorm = 3,      // C is not stored; rowsq[z][m] = sum over segment 0 of opA(m, k)^2 and
-                     // rowdot[z][tile_n][wave column][m] = alpha * sum over the tile's n of
-                     // C(m, n) * add(m, n) (bf16, both operands K-contiguous; z = split index)
+  kEpiNorm = 3,      // C is not stored; rowsq[z][m] = sum over segment 0 of opA(m, k)^2
+                     // and rowdot[z][tile_n][wave column][m] = alpha * sum over the tile's
+                     // n of C(m, n) * add(m, n) (bf16, both operands K-contiguous;
+                     // z = split index)
 };
 
 struct GemmProblem {
@@ -61,6 +62,13 @@ struct GemmPlan {
 // and operand layout.
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc = true, bool bkc = true);
 
+// Tile configuration and split-K factor of the norm's projection P = [W0 | B | B] [A | G]^T
+// (M = d_out, N = r, K = d_in + 2r; ld_max = the largest row stride of its operands).
+GemmPlan plan_norm_projection(int64_t M, int64_t N, int64_t K, int64_t ld_max);
+
+// Tile-rows of a GEMM with M rows on tile configuration cfg.
+int64_t gemm_tile_rows(int cfg, int64_t M);
+
 // Row-dot partials per split of a kEpiNorm GEMM with N columns on tile configuration cfg.
 int64_t gemm_col_slots(int cfg, int64_t N);
 
@@ -71,6 +79,23 @@ size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype, bool akc =
 // Enqueue C = sum over segments; picks the tile configuration from the shape.
 hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* label);
 
+
+// Gram matrix G = A A^T of a bf16 A [r, d_in] (csrc/gram.hip): float32 partial
+// sums of the upper-triangle 64 x 64 tiles over K splits, then a finisher that
+// writes scale * G as a bf16 hi + lo pair (exactly symmetric) and zeroes
+// `nzero` counters for later kernels of the call.
+struct GramPlan {
+  int64_t tiles;       // upper-triangle tiles
+  int64_t splits;      // K chunks
+  int64_t kchunk;      // K extent of one chunk
+  size_t part_bytes;   // float32 partial sums
+};
+GramPlan gram_bf16_plan(int64_t r, int64_t d_in);
+hipError_t gram_bf16(const void* A, int64_t r, int64_t d_in, const GramPlan& g, float* part,
+                     hipStream_t st);
+hipError_t gram_bf16_finish(const float* part, const GramPlan& g, int64_t r, float scale,
+                            void* g_hi, void* g_lo, uint32_t* zero, int64_t nzero,
+                            hipStream_t st);
 
 // scale * (sum of r x r partial sums); bf16: written as a hi + lo bf16 pair.
 hipError_t gram_finalize(const float* part, int splits, int64_t r, float scale, int dtype,

@@ -68,11 +68,21 @@ static hipError_t launch(const char* label, hipStream_t st) {
 namespace dora {
 GemmPlan plan_gemm(int64_t, int64_t, int64_t, int, bool, bool) { return {2, 2}; }
 int64_t gemm_col_slots(int, int64_t N) { return (N + 127) / 128 * 2; }
+GemmPlan plan_norm_projection(int64_t, int64_t, int64_t, int64_t) { return {2, 2}; }
+int64_t gemm_tile_rows(int, int64_t M) { return (M + 127) / 128; }
 size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t, int, bool, bool) {
   return (size_t)2 * M * N * 4;
 }
 hipError_t gemm(const GemmProblem&, int, hipStream_t st, const char* label) {
   return launch(label, st);
+}
+GramPlan gram_bf16_plan(int64_t r, int64_t) { return GramPlan{1, 1, 64, (size_t)(r * r * 4)}; }
+hipError_t gram_bf16(const void*, int64_t, int64_t, const GramPlan&, float*, hipStream_t st) {
+  return launch("gram_AAt", st);
+}
+hipError_t gram_bf16_finish(const float*, const GramPlan&, int64_t, float, void*, void*, uint32_t*,
+                            int64_t, hipStream_t st) {
+  return launch("gram_finalize", st);
 }
 hipError_t gram_finalize(const float*, int, int64_t, float, int, void*, void*, hipStream_t st,
                          const char* label) {
