@@ -16,8 +16,10 @@ from events between consecutive back-to-back steps (``step_spread`` summarises
 the same series).  ``roofline`` covers the dominant kernel (largest share of
 the step), timed with HIP events on the library's launch stream in a separate
 pass; ``kernels`` lists every kernel of the step the same way.  ``norm`` is the
-whole factored-norm chain (µs, algorithmic GB/s against 8 TB/s, fraction of
-its max(HBM, MFMA) bound); ``compose_fwd`` times the standalone one-pass
+whole factored-norm chain timed as back-to-back dora_norm calls (µs,
+algorithmic GB/s against 8 TB/s, fraction of its max(HBM, MFMA) bound;
+``norm_kernels`` sums the chain's kernels from the per-kernel pass, whose
+events add a few µs to every short kernel); ``compose_fwd`` times the standalone one-pass
 compose kernel in the same process (the default path runs the compose as the
 forward GEMM's epilogue) and ``compose_bwd`` the backward's.  ``configs``
 gives the forward of the other synthetic layers (a tiny float32 layer, the
@@ -269,6 +271,18 @@ def norm_summary(timing, steps, d_out, d_in, r, e=2):
             "bound": "max(bytes at 8 TB/s, flops at 2.5 PFLOP/s)"}
 
 
+def norm_call_summary(ms, per_ms, d_out, d_in, r, e=2):
+    """dora_norm timed as one call (events between back-to-back calls): the norm
+    chain without the per-kernel events of the kernel table."""
+    nbytes, flops = norm_work(d_out, d_in, r, e)
+    us = ms * 1e3
+    bound_us = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFS * 1e12)) * 1e6
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "per_call": step_stats(per_ms), "gbps": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bound_us": round(bound_us, 2),
+            "frac_of_bound": round(bound_us / us, 4)}
+
+
 def step_stats(per_ms):
     import numpy as np
     return {"median_us": round(float(np.median(per_ms)) * 1e3, 2),
@@ -324,6 +338,16 @@ def forward_config(torch, np, ops, synth, name, dev, steps, warmup, tensors=None
     for _ in range(warmup):
         fwd()
     ms, per = timed_series(torch, fwd, steps)
+    # the factored norm alone, as one call (no per-kernel events between its launches)
+    ws_n = torch.empty(max(1, ops.workspace_bytes(d_out, d_in, r, T, tdt, 0)), dtype=torch.uint8,
+                       device=dev)
+
+    def nrm():
+        ops.dora_norm(d["W0"], d["A"], d["B"], s, out=norm, workspace=ws_n)
+
+    for _ in range(warmup):
+        nrm()
+    norm_ms, norm_per = timed_series(torch, nrm, steps)
     ops.timing_enable(True)
     for _ in range(steps):
         fwd()
@@ -340,6 +364,7 @@ def forward_config(torch, np, ops, synth, name, dev, steps, warmup, tensors=None
             "algorithmic_flops": fwd_flops + nf,
             "tflops": round((fwd_flops + nf) / (ms * 1e-3) / 1e12, 2),
             "norm": norm_summary(timing, steps, d_out, d_in, r, e),
+            "norm_call": norm_call_summary(norm_ms, norm_per, d_out, d_in, r, e),
             "kernels": kernel_table(timing, steps, work, {}, None, flop_peak)}
 
 
@@ -556,6 +581,21 @@ def main():
         if peaks:
             roof["frac_of_measured"] = round(achieved / peaks["hbm_stream_GBs"], 4)
 
+    norm_call = None
+    if not args.cold and not args.graph:
+        ws_n = torch.empty(max(1, ops.workspace_bytes(d_out, d_in, r, T, tdt, 0)),
+                           dtype=torch.uint8, device=dev)
+        nrm_out = torch.empty(d_out, dtype=torch.float32, device=dev)
+
+        def nrm():
+            ops.dora_norm(d["W0"], d["A"], d["B"], s, out=nrm_out, workspace=ws_n)
+
+        for _ in range(max(3, args.warmup)):
+            nrm()
+        n_ms, n_per = timed_series(torch, nrm, max(10, args.steps))
+        norm_call = norm_call_summary(n_ms, n_per, d_out, d_in, r, e)
+        del ws_n
+
     configs = None
     if backward and not args.no_configs and not args.cold and not args.graph and not flags:
         configs = {}
@@ -596,7 +636,8 @@ def main():
                    "launch": "HIP graph replay" if args.graph else "eager",
                    "parallelism": "dp1"},
         "roofline": roof,
-        "norm": norm_summary(timing, args.steps, d_out, d_in, r, e),
+        "norm": norm_call,
+        "norm_kernels": norm_summary(timing, args.steps, d_out, d_in, r, e),
         "compose_fwd": compose_fwd,
         "compose_bwd": kernels.get("compose_bwd"),
         "cpu_baseline": cpu,

@@ -64,7 +64,7 @@ struct KArgs {
   const void* add;
   int64_t ld_add;
   float* rowsq;          // kEpiNorm: [nsplit][M] sums of squares of opA over segment 0
-  float* rowdot;         // kEpiNorm: [nsplit][tiles_n][WN][M] row dots of alpha*C with `add`
+  float* rowdot;         // kEpiNorm: [nsplit][tiles_n][M] row dots of alpha*C with `add`
   int nsplit;            // K splits (the bf16 kernels' grid is tiles x nsplit, 1-D)
 };
 
@@ -823,7 +823,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
         if (lane < 32 && m < M) p.rowsq[(int64_t)split * M + m] = v;
       }
     }
-    const int64_t slot = ((int64_t)split * p.tiles_n + tc.y) * WN + wn;
+    const int64_t slot = (int64_t)split * p.tiles_n + tc.y;
     // C itself is not stored: each lane dots its accumulators with the rows
     // of `add` at the same (m, n) (in-lane over j, g, e, then the two lanes
     // that share a row), one partial per split, column tile and wave column.
@@ -849,12 +849,27 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
         }
       }
     }
+    // The WN wave columns hold partial dots of the same rows: they meet in LDS
+    // (free after the K loop's final barrier) and the first wave column adds
+    // them in wave-column order, one partial per split and column tile.
+    float* red = reinterpret_cast<float*>(smem);   // [WN][BM]
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       float v = dot[i];
       v += __shfl_xor(v, 32);
-      const int m = m0 + wm * TM + i * 32 + lane;
-      if (lane < 32 && m < M) p.rowdot[slot * M + m] = p.alpha * v;
+      if (lane < 32) red[wn * BM + wm * TM + i * 32 + lane] = v;
+    }
+    __syncthreads();
+    if (wn == 0) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int rr = wm * TM + i * 32 + lane;
+        const int m = m0 + rr;
+        float v = red[rr];
+#pragma unroll
+        for (int w = 1; w < WN; ++w) v += red[w * BM + rr];
+        if (lane < 32 && m < M) p.rowdot[slot * M + m] = p.alpha * v;
+      }
     }
     return;
   }
@@ -1002,6 +1017,7 @@ constexpr Cfg kCfgs[] = {
     {256, 128, 4, 2},   // 5: 8 waves, 64x64 per wave
     {128, 384, 2, 4},   // 6: 8 waves, 64x96 per wave (N = rank 384 in one tile)
     {384, 128, 4, 2},   // 7: 8 waves, 96x64 per wave (M = rank 384 in one tile)
+    {128, 192, 2, 2},   // 8: 4 waves, 64x96 per wave (two workgroups per CU; K-contiguous only)
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -1043,15 +1059,24 @@ hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStre
   return hipGetLastError();
 }
 
+// An M/N-contiguous operand is copied straight to LDS when its tile side is a
+// multiple of 128 (whole 16-chunk groups per k-row) and through registers
+// below 128 rows; other widths take K-contiguous operands only.
+template <int R>
+constexpr bool kMcOk = R % 128 == 0 || (R < 128 && R % 64 == 0);
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_layout(bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
                          hipStream_t st) {
   if (akc && bkc) return launch_bf16<BM, BN, WM, WN, true, true>(a, epi, out_f32, grid, st);
-  if (akc && !bkc) return launch_bf16<BM, BN, WM, WN, true, false>(a, epi, out_f32, grid, st);
-  // two register-staged operands do not fit beside a 256 x 256 tile's accumulators
-  // (transposed operands of 128 rows or more are copied straight to LDS)
-  if constexpr (BM * BN <= 256 * 128 || (DORA_MC_DIRECT && BM >= 128 && BN >= 128))
-    if (!akc && !bkc) return launch_bf16<BM, BN, WM, WN, false, false>(a, epi, out_f32, grid, st);
+  if constexpr (kMcOk<BN>) {
+    if (akc && !bkc) return launch_bf16<BM, BN, WM, WN, true, false>(a, epi, out_f32, grid, st);
+    // two register-staged operands do not fit beside a 256 x 256 tile's accumulators
+    // (transposed operands of 128 rows or more are copied straight to LDS)
+    if constexpr (kMcOk<BM> &&
+                  (BM * BN <= 256 * 128 || (DORA_MC_DIRECT && BM >= 128 && BN >= 128)))
+      if (!akc && !bkc) return launch_bf16<BM, BN, WM, WN, false, false>(a, epi, out_f32, grid, st);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -1066,6 +1091,7 @@ hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool
     case 5: return launch_layout<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 6: return launch_layout<128, 384, 2, 4>(akc, bkc, a, epi, out_f32, grid, st);
     case 7: return launch_layout<384, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 8: return launch_layout<128, 192, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1189,7 +1215,7 @@ int64_t gemm_tile_rows(int cfg, int64_t M) {
 
 int64_t gemm_col_slots(int cfg, int64_t N) {
   if (cfg < 0 || cfg >= kNumCfgs) return 0;
-  return cdiv64(N, kCfgs[cfg].bn) * kCfgs[cfg].wn;
+  return cdiv64(N, kCfgs[cfg].bn);
 }
 
 size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bkc) {

@@ -204,7 +204,8 @@ GramPlan gram_bf16_plan(int64_t r, int64_t d_in) {
   g.tiles = nt * (nt + 1) / 2;
   // about 320 workgroups (two fit a CU), K chunks a whole number of stages
   const int64_t span = kGK;
-  int64_t splits = std::max<int64_t>(1, (320 + g.tiles - 1) / g.tiles);
+  // (at most 32 splits: the finisher adds every split of an element in turn)
+  int64_t splits = std::max<int64_t>(1, std::min<int64_t>(32, (320 + g.tiles - 1) / g.tiles));
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, cdiv(d_in, span)));
   g.kchunk = cdiv(cdiv(d_in, splits), span) * span;
   g.splits = cdiv(d_in, g.kchunk);

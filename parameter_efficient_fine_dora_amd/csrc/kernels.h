@@ -22,7 +22,7 @@ enum Epilogue : int {
   kEpiCompose = 1,   // C = z + (g - 1) z with z = alpha * acc, g_n = m_n / max(norm_n, eps)
   kEpiMerge = 2,     // C = g_m (add + alpha * acc) with g_m = m_m / max(norm_m, eps) per ROW
   kEpiNorm = 3,      // C is not stored; rowsq[z][m] = sum over segment 0 of opA(m, k)^2
-                     // and rowdot[z][tile_n][wave column][m] = alpha * sum over the tile's
+                     // and rowdot[z][tile_n][m] = alpha * sum over the tile's
                      // n of C(m, n) * add(m, n) (bf16, both operands K-contiguous;
                      // z = split index)
 };
