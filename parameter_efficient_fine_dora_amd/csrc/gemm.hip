@@ -579,8 +579,12 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / W
 // memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32>
+// NSEG: the most K segments the kernel walks (2, or 3 for the norm's projection
+// and the undetached-gradient products): every segment's pointers, strides
+// and bounds live in scalar registers, which the largest tiles have to spare.
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32, int NSEG>
 __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
+  static_assert(NSEG == 2 || NSEG == 3, "two or three K segments");
   constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MB = TM / 32, NB = TN / 32;
@@ -622,12 +626,13 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   const int split = __builtin_amdgcn_readfirstlane(tc.z);
   const int kt_lo = split * p.kt_per_split;
   const int kt_hi = min(kt_lo + p.kt_per_split, p.kt_total);
-  const int kt_end0 = p.kt_end[0], kt_end1 = p.kt_end[1], kt_end2 = p.kt_end[2];
-  const uint16_t *a0 = p.a[0], *a1 = p.a[1], *a2 = p.a[2];
-  const uint16_t *b0 = p.b[0], *b1 = p.b[1], *b2 = p.b[2];
-  const int64_t lda0 = p.lda[0], lda1 = p.lda[1], lda2 = p.lda[2];
-  const int64_t ldb0 = p.ldb[0], ldb1 = p.ldb[1], ldb2 = p.ldb[2];
-  const int K0 = p.K[0], K1 = p.K[1], K2 = p.K[2];
+  constexpr bool k3 = NSEG == 3;
+  const int kt_end0 = p.kt_end[0], kt_end1 = p.kt_end[1], kt_end2 = k3 ? p.kt_end[2] : 0;
+  const uint16_t *a0 = p.a[0], *a1 = p.a[1], *a2 = k3 ? p.a[2] : nullptr;
+  const uint16_t *b0 = p.b[0], *b1 = p.b[1], *b2 = k3 ? p.b[2] : nullptr;
+  const int64_t lda0 = p.lda[0], lda1 = p.lda[1], lda2 = k3 ? p.lda[2] : 0;
+  const int64_t ldb0 = p.ldb[0], ldb1 = p.ldb[1], ldb2 = k3 ? p.ldb[2] : 0;
+  const int K0 = p.K[0], K1 = p.K[1], K2 = k3 ? p.K[2] : 0;
 
   f32x16 acc[MB][NB];
 #pragma unroll
@@ -759,7 +764,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   // most two restarts per launch), so within a segment the copy state is
   // loop-invariant.
 #pragma unroll 1
-  for (int seg = 0; seg < 3; ++seg) {
+  for (int seg = 0; seg < NSEG; ++seg) {
     const int s_lo = seg == 0 ? 0 : (seg == 1 ? kt_end0 : kt_end1);
     const int s_hi = seg == 0 ? kt_end0 : (seg == 1 ? kt_end1 : kt_end2);
     const int lo = max(kt_lo, s_lo), hi = min(kt_hi, s_hi);
@@ -1021,42 +1026,44 @@ constexpr Cfg kCfgs[] = {
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32, int NSEG>
+hipError_t launch_one(const KArgs& a, dim3 grid, hipStream_t st) {
+  if (a.nseg > NSEG) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, EPI, OUT_F32, NSEG>), grid,
+                     dim3(WM * WN * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+// The store epilogues come with two or three segments, picked by the problem.
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, bool OUT_F32>
+hipError_t launch_store(const KArgs& a, dim3 grid, hipStream_t st) {
+  if (a.nseg > 2)
+    return launch_one<BM, BN, WM, WN, AKC, BKC, kEpiStore, OUT_F32, 3>(a, grid, st);
+  return launch_one<BM, BN, WM, WN, AKC, BKC, kEpiStore, OUT_F32, 2>(a, grid, st);
+}
+
 template <int BM, int BN, int WM, int WN, bool AKC, bool BKC>
 hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStream_t st) {
-  const dim3 block(WM * WN * 64);
   if (out_f32) {
     if constexpr (AKC && BKC) {   // the norm's projection: W0 and A are K-contiguous
-      if (epi == kEpiNorm) {
-        hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiNorm, true>), grid,
-                           block, 0, st, a);
-        return hipGetLastError();
-      }
+      if (epi == kEpiNorm)
+        return launch_one<BM, BN, WM, WN, AKC, BKC, kEpiNorm, true, 3>(a, grid, st);
     }
     if (epi == kEpiNorm) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, true>), grid, block, 0,
-                       st, a);
-    return hipGetLastError();
+    return launch_store<BM, BN, WM, WN, AKC, BKC, true>(a, grid, st);
   }
   if constexpr (AKC && BKC) {   // the compose epilogue belongs to the forward (K-contiguous) GEMM
-    if (epi == kEpiCompose) {
-      hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiCompose, false>), grid,
-                         block, 0, st, a);
-      return hipGetLastError();
-    }
+    if (epi == kEpiCompose)
+      return launch_one<BM, BN, WM, WN, AKC, BKC, kEpiCompose, false, 2>(a, grid, st);
     if (epi != kEpiStore) return hipErrorInvalidValue;
   } else if constexpr (AKC && !BKC) {   // the merge epilogue belongs to B . A
-    if (epi == kEpiMerge) {
-      hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiMerge, false>), grid,
-                         block, 0, st, a);
-      return hipGetLastError();
-    }
+    if (epi == kEpiMerge)
+      return launch_one<BM, BN, WM, WN, AKC, BKC, kEpiMerge, false, 2>(a, grid, st);
     if (epi != kEpiStore) return hipErrorInvalidValue;
   } else {
     if (epi != kEpiStore) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, kEpiStore, false>), grid, block, 0,
-                     st, a);
-  return hipGetLastError();
+  return launch_store<BM, BN, WM, WN, AKC, BKC, false>(a, grid, st);
 }
 
 // An M/N-contiguous operand is copied straight to LDS when its tile side is a
