@@ -100,8 +100,12 @@ __device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t off) {
 
 // K-contiguous operand, R rows x 64 k per stage, copied straight into LDS with
 // buffer_load ... lds: one wave instruction fills 8 rows x 128 B, lane l takes
-// row l/8 and physical chunk l%8, i.e. logical chunk (l%8) ^ swz(row).  Rows
-// past the operand are beyond the descriptor's records and read as zeros.
+// row l/8 and physical chunk l%8, i.e. logical chunk (l%8) ^ swz(row).  Every
+// instruction has its own per-lane offset (its row and chunk), set once per
+// segment, and a step only supplies the K position as the scalar offset.  The
+// hardware range check covers the per-lane offset only (the scalar offset is
+// added after it), so rows past the operand, beyond the descriptor's records,
+// read as zeros, and the K position (< ld) keeps a valid row inside its row.
 template <int R, int NW>
 struct CopyKC {
   static constexpr int kInstr = R / 8 / NW;   // 16-byte copies per lane and stage
@@ -109,18 +113,8 @@ struct CopyKC {
   // Per-lane offsets reach (R - 1) * ld * 2 + 112; the planner keeps R * ld * 2
   // below 2^31 (always true for R <= 256, since every stride is below 2^22).
   static_assert(R <= 384, "tile rows");
-  // Instruction i of a wave fills rows (wave + i*NW)*8 .. +8.  With NW a
-  // multiple of 8 every instruction sees the same swizzle, so one per-lane
-  // offset serves them all: on a full tile the row step goes into the scalar
-  // offset.  The hardware range check covers the per-lane offset only (the
-  // scalar offset is added after it), so on a partial tile the row step goes
-  // into the per-lane offset instead and rows past the operand read as zeros.
-  static constexpr bool kOne = NW % 8 == 0;
-  static constexpr int kOffs = kOne ? 1 : kInstr;
   Rsrc rs;                 // tile base at k = 0, records = valid rows * ld * 2
-  uint32_t off[kOffs];     // row * ld * 2 + chunk * 16 (< 2^31: every dimension is < 2^22)
-  int step;                // bytes between instruction i and i+1 when kOne
-  bool full;               // kOne: all R rows of the tile lie inside the operand (wave-uniform)
+  uint32_t off[kInstr];    // row * ld * 2 + chunk * 16
   __device__ __forceinline__ static int row_of(int i, int wave, int lane) {
     return (wave + i * NW) * 8 + (lane >> 3);
   }
@@ -128,11 +122,9 @@ struct CopyKC {
                                           int wave, int lane, int) {
     int64_t rows = nrows - row0;
     if (rows > R) rows = R;
-    full = rows == R;
     rs = make_rsrc(p + (int64_t)row0 * ld, rows * ld * 2);
-    step = NW * 8 * (int)(ld * 2);
 #pragma unroll
-    for (int i = 0; i < kOffs; ++i) {
+    for (int i = 0; i < kInstr; ++i) {
       const int row = row_of(i, wave, lane);
       const int kc = (lane & 7) ^ swz(row);
       off[i] = (uint32_t)row * (uint32_t)(ld * 2) + (uint32_t)kc * 16u;
@@ -141,14 +133,13 @@ struct CopyKC {
   // Step kt (relative to the segment) into the stage tile.  On a partial step
   // the chunks at or beyond K read as zeros: kOob plus the scalar offset stays
   // below 2^32 and beyond every record count.
-  template <bool TAIL, bool ROWSTEP_IN_SOFF>
-  __device__ __forceinline__ void issue_rows(uint8_t* lds_tile, int kt, int K, int wave,
-                                             int lane) {
+  template <bool TAIL>
+  __device__ __forceinline__ void issue(uint8_t* lds_tile, int kt, int K, int wave, int lane,
+                                        int) {
     const int kbytes = kt * kRowBytes;
 #pragma unroll
     for (int i = 0; i < kInstr; ++i) {
-      // row * ld * 2 + chunk * 16 < R * 2^23 <= 2^31: the per-lane sum cannot wrap
-      uint32_t o = kOne ? (ROWSTEP_IN_SOFF ? off[0] : off[0] + (uint32_t)(i * step)) : off[i];
+      uint32_t o = off[i];
       if (TAIL) {
         const int row = row_of(i, wave, lane);
         const int kc = (lane & 7) ^ swz(row);
@@ -156,16 +147,8 @@ struct CopyKC {
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)(lds_tile + (wave + i * NW) * 8 * kRowBytes),
-          16, (int)o, kbytes + ((kOne && ROWSTEP_IN_SOFF) ? i * step : 0), 0, 0);
+          16, (int)o, kbytes, 0, 0);
     }
-  }
-  template <bool TAIL>
-  __device__ __forceinline__ void issue(uint8_t* lds_tile, int kt, int K, int wave, int lane,
-                                        int) {
-    if (!kOne || full)
-      issue_rows<TAIL, true>(lds_tile, kt, K, wave, lane);
-    else
-      issue_rows<TAIL, false>(lds_tile, kt, K, wave, lane);
   }
   __device__ __forceinline__ void commit(uint8_t*, int) {}
 };
