@@ -565,9 +565,11 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 // NSEG: the most K segments the kernel walks (2, or 3 for the norm's projection
 // and the undetached-gradient products): every segment's pointers, strides
 // and bounds live in scalar registers, which the largest tiles have to spare.
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32, int NSEG>
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32, int NSEG,
+          int S>
 __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   static_assert(NSEG == 2 || NSEG == 3, "two or three K segments");
+  static_assert(S >= 2 && S <= 4, "two to four stages");
   constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MB = TM / 32, NB = TN / 32;
@@ -575,14 +577,16 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   using CA = CopyOp<BM, NT, AKC>;
   using CB = CopyOp<BN, NT, BKC>;
   constexpr bool kRegs = CA::kRegs || CB::kRegs;
+  static_assert(S == 2 || !kRegs, "register-staged copies take the two-stage pipeline");
   constexpr bool kTrA = CA::kTr, kTrB = CB::kTr;
-  // LDS.  With an operand read by the transposing read, one object per operand
-  // and stage: kept apart, they let the compiler see that a stage's fragment
-  // reads cannot touch the other stage, which the copies in flight are
-  // filling (without that it waits for every copy before a transposing read).
-  // Otherwise one object [A stage 0 | A stage 1 | B stage 0 | B stage 1], so
-  // that every fragment read is a per-lane base plus an immediate offset.
-  constexpr bool kSplit = kTrA || kTrB;
+  // LDS.  With an operand read by the transposing read, or more than two
+  // stages, one object per operand and stage: kept apart, they let the compiler
+  // see that a stage's fragment reads cannot touch the other stages, which the
+  // copies in flight are filling (without that it waits for every copy before
+  // a transposing read).  Otherwise one object [A stage 0 | A stage 1 | B
+  // stage 0 | B stage 1], so that every fragment read is a per-lane base plus
+  // an immediate offset.
+  constexpr bool kSplit = kTrA || kTrB || S > 2;
   constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
   constexpr int BBASE = kSplit ? 0 : 2 * ABYTES;   // B's offset within its object
   static_assert(kSplit || (ABYTES + (MB > 2 ? 64 * kRowBytes : 0) < 65536 &&
@@ -592,6 +596,11 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[kSplit ? ABYTES : 1];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kSplit ? BBYTES : 1];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[kSplit ? BBYTES : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[S > 2 ? ABYTES : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[S > 2 ? BBYTES : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA3[S > 3 ? ABYTES : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB3[S > 3 ? BBYTES : 1];
+  static_assert(S * (ABYTES + BBYTES) <= 160 * 1024, "stages must fit the LDS");
   // bf16 epilogue: each wave stages 32 rows of its tile at a time in a region
   // of its own.
   constexpr int kStageLd = TN + 8;
@@ -663,8 +672,10 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
 
   // Stage SB of each operand (B's offset BBASE within the object is in the
   // fragment bases and added for the copies).
-#define DORA_A(SB) (kSplit ? ((SB) ? sA1 : smem) : smem + (SB) * ABYTES)
-#define DORA_B(SB) (kSplit ? ((SB) ? sB1 : sB0) : smem + (SB) * BBYTES)
+#define DORA_A(SB) \
+  (kSplit ? ((SB) == 0 ? smem : (SB) == 1 ? sA1 : (SB) == 2 ? sA2 : sA3) : smem + (SB) * ABYTES)
+#define DORA_B(SB) \
+  (kSplit ? ((SB) == 0 ? sB0 : (SB) == 1 ? sB1 : (SB) == 2 ? sB2 : sB3) : smem + (SB) * BBYTES)
   // Copies of segment step KR into stage SB.
 #define DORA_FETCH(KR, SB)                                                                 \
   do {                                                                                     \
@@ -743,9 +754,8 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
     }                                                                                      \
   } while (0)
 
-  // Segments one after the other; the two-stage pipeline restarts at each (at
-  // most two restarts per launch), so within a segment the copy state is
-  // loop-invariant.
+  // Segments one after the other; the pipeline restarts at each (at most two
+  // restarts per launch), so within a segment the copy state is loop-invariant.
 #pragma unroll 1
   for (int seg = 0; seg < NSEG; ++seg) {
     const int s_lo = seg == 0 ? 0 : (seg == 1 ? kt_end0 : kt_end1);
@@ -762,10 +772,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
     cb.prepare(seg == 0 ? b0 : (seg == 1 ? b1 : b2), seg == 0 ? ldb0 : (seg == 1 ? ldb1 : ldb2),
                n0, N, Ks, wave, lane, tid);
     const int r_lo = lo - s_lo, r_hi = hi - s_lo;
-    DORA_FETCH(r_lo, 0);
-    DORA_COMMIT(0);
-    wait_vmem();
-    barrier_nofence();
+    // Two stages: the copies of step kr + 1 fly while step kr is multiplied.
 #define DORA_STAGES(SQ)                                                                    \
   for (int kr = r_lo; kr < r_hi; kr += 2) {                                                \
     if (kr + 1 < r_hi) DORA_FETCH(kr + 1, 1);                                              \
@@ -785,7 +792,39 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
     // so the compiler keeps the other waves' loop free of it); the sums of
     // segment 0 are kept when it ends.
     const bool sq_w = kRowSq && wn == 0 && tc.y == 0;
-    DORA_STAGES(sq_w)
+    if constexpr (S == 2) {
+      DORA_FETCH(r_lo, 0);
+      DORA_COMMIT(0);
+      wait_vmem();
+      barrier_nofence();
+      DORA_STAGES(sq_w)
+    } else {
+      // A ring of S stages: the copies of the next S - 1 steps fly while a step
+      // is multiplied.  Step q lives in slot (q - r_lo) % S; it has landed once
+      // at most the copies of the steps issued after it are outstanding (vmcnt
+      // retires loads in order), and the barrier after that wait also tells
+      // that every wave is done with slot (q - 1) % S, which then takes step
+      // q + S - 1.
+      constexpr int kPS = CA::kInstr + CB::kInstr;   // copy instructions per step and wave
+#pragma unroll
+      for (int j = 0; j < S - 1; ++j)
+        if (r_lo + j < r_hi) DORA_FETCH(r_lo + j, j);
+      for (int kr = r_lo; kr < r_hi; kr += S) {
+#pragma unroll
+        for (int J = 0; J < S; ++J) {
+          const int q = kr + J;
+          if (q >= r_hi) break;
+          const int later = min(S - 2, r_hi - 1 - q);
+          if (S > 3 && later >= 2) wait_vmem_le<(S > 3 ? 2 * kPS : 0)>();
+          else if (later >= 1) wait_vmem_le<kPS>();
+          else wait_vmem_le<0>();
+          barrier_nofence();
+          if (q + S - 1 < r_hi) DORA_FETCH(q + S - 1, (J + S - 1) % S);
+          DORA_MMA(J, sq_w);
+        }
+      }
+      barrier_nofence();   // every slot read before the next segment or the epilogue reuses LDS
+    }
     if (kRowSq && seg == 0) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) sq0[i] = sq[0][i] + sq[1][i];
@@ -992,61 +1031,63 @@ __global__ __launch_bounds__(256) void dora_splitk_reduce(const float* part, int
 
 // ---- host-side dispatch -----------------------------------------------------
 
-// Tile configurations: BM x BN workgroup tile, WM x WN waves.
+// Tile configurations: BM x BN workgroup tile, WM x WN waves, pipeline stages.
 struct Cfg {
-  int bm, bn, wm, wn;
+  int bm, bn, wm, wn, st;
 };
 constexpr Cfg kCfgs[] = {
-    {256, 256, 2, 4},   // 0: 8 waves, 128x64 per wave
-    {256, 128, 2, 2},   // 1: 4 waves, 128x64 per wave
-    {128, 128, 2, 2},   // 2: 4 waves, 64x64 per wave
-    {128, 256, 2, 2},   // 3: 4 waves, 64x128 per wave
-    {64, 64, 2, 2},     // 4: 4 waves, 32x32 per wave
-    {256, 128, 4, 2},   // 5: 8 waves, 64x64 per wave
-    {128, 384, 2, 4},   // 6: 8 waves, 64x96 per wave (N = rank 384 in one tile)
-    {384, 128, 4, 2},   // 7: 8 waves, 96x64 per wave (M = rank 384 in one tile)
-    {128, 192, 2, 2},   // 8: 4 waves, 64x96 per wave (two workgroups per CU; K-contiguous only)
+    {256, 256, 2, 4, 2},   // 0: 8 waves, 128x64 per wave
+    {256, 128, 2, 2, 2},   // 1: 4 waves, 128x64 per wave
+    {128, 128, 2, 2, 2},   // 2: 4 waves, 64x64 per wave
+    {128, 256, 2, 2, 2},   // 3: 4 waves, 64x128 per wave
+    {64, 64, 2, 2, 2},     // 4: 4 waves, 32x32 per wave
+    {256, 128, 4, 2, 2},   // 5: 8 waves, 64x64 per wave
+    {128, 384, 2, 4, 2},   // 6: 8 waves, 64x96 per wave (N = rank 384 in one tile)
+    {384, 128, 4, 2, 2},   // 7: 8 waves, 96x64 per wave (M = rank 384 in one tile)
+    {128, 192, 2, 2, 2},   // 8: 4 waves, 64x96 per wave (two workgroups per CU; K-contiguous only)
+    {128, 128, 2, 2, 3},   // 9: as 2 with three stages (one workgroup per CU)
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI, bool OUT_F32, int NSEG>
+template <int BM, int BN, int WM, int WN, int S, bool AKC, bool BKC, int EPI, bool OUT_F32,
+          int NSEG>
 hipError_t launch_one(const KArgs& a, dim3 grid, hipStream_t st) {
   if (a.nseg > NSEG) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, EPI, OUT_F32, NSEG>), grid,
+  hipLaunchKernelGGL((dora_gemm_bf16<BM, BN, WM, WN, AKC, BKC, EPI, OUT_F32, NSEG, S>), grid,
                      dim3(WM * WN * 64), 0, st, a);
   return hipGetLastError();
 }
 
 // The store epilogues come with two or three segments, picked by the problem.
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, bool OUT_F32>
+template <int BM, int BN, int WM, int WN, int S, bool AKC, bool BKC, bool OUT_F32>
 hipError_t launch_store(const KArgs& a, dim3 grid, hipStream_t st) {
   if (a.nseg > 2)
-    return launch_one<BM, BN, WM, WN, AKC, BKC, kEpiStore, OUT_F32, 3>(a, grid, st);
-  return launch_one<BM, BN, WM, WN, AKC, BKC, kEpiStore, OUT_F32, 2>(a, grid, st);
+    return launch_one<BM, BN, WM, WN, S, AKC, BKC, kEpiStore, OUT_F32, 3>(a, grid, st);
+  return launch_one<BM, BN, WM, WN, S, AKC, BKC, kEpiStore, OUT_F32, 2>(a, grid, st);
 }
 
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC>
+template <int BM, int BN, int WM, int WN, int S, bool AKC, bool BKC>
 hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStream_t st) {
   if (out_f32) {
     if constexpr (AKC && BKC) {   // the norm's projection: W0 and A are K-contiguous
       if (epi == kEpiNorm)
-        return launch_one<BM, BN, WM, WN, AKC, BKC, kEpiNorm, true, 3>(a, grid, st);
+        return launch_one<BM, BN, WM, WN, S, AKC, BKC, kEpiNorm, true, 3>(a, grid, st);
     }
     if (epi == kEpiNorm) return hipErrorInvalidValue;
-    return launch_store<BM, BN, WM, WN, AKC, BKC, true>(a, grid, st);
+    return launch_store<BM, BN, WM, WN, S, AKC, BKC, true>(a, grid, st);
   }
   if constexpr (AKC && BKC) {   // the compose epilogue belongs to the forward (K-contiguous) GEMM
     if (epi == kEpiCompose)
-      return launch_one<BM, BN, WM, WN, AKC, BKC, kEpiCompose, false, 2>(a, grid, st);
+      return launch_one<BM, BN, WM, WN, S, AKC, BKC, kEpiCompose, false, 2>(a, grid, st);
     if (epi != kEpiStore) return hipErrorInvalidValue;
   } else if constexpr (AKC && !BKC) {   // the merge epilogue belongs to B . A
     if (epi == kEpiMerge)
-      return launch_one<BM, BN, WM, WN, AKC, BKC, kEpiMerge, false, 2>(a, grid, st);
+      return launch_one<BM, BN, WM, WN, S, AKC, BKC, kEpiMerge, false, 2>(a, grid, st);
     if (epi != kEpiStore) return hipErrorInvalidValue;
   } else {
     if (epi != kEpiStore) return hipErrorInvalidValue;
   }
-  return launch_store<BM, BN, WM, WN, AKC, BKC, false>(a, grid, st);
+  return launch_store<BM, BN, WM, WN, S, AKC, BKC, false>(a, grid, st);
 }
 
 // An M/N-contiguous operand is copied straight to LDS when its tile side is a
@@ -1055,17 +1096,17 @@ hipError_t launch_bf16(const KArgs& a, int epi, bool out_f32, dim3 grid, hipStre
 template <int R>
 constexpr bool kMcOk = R % 128 == 0 || (R < 128 && R % 64 == 0);
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int S>
 hipError_t launch_layout(bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
                          hipStream_t st) {
-  if (akc && bkc) return launch_bf16<BM, BN, WM, WN, true, true>(a, epi, out_f32, grid, st);
+  if (akc && bkc) return launch_bf16<BM, BN, WM, WN, S, true, true>(a, epi, out_f32, grid, st);
   if constexpr (kMcOk<BN>) {
-    if (akc && !bkc) return launch_bf16<BM, BN, WM, WN, true, false>(a, epi, out_f32, grid, st);
+    if (akc && !bkc) return launch_bf16<BM, BN, WM, WN, S, true, false>(a, epi, out_f32, grid, st);
     // two register-staged operands do not fit beside a 256 x 256 tile's accumulators
     // (transposed operands of 128 rows or more are copied straight to LDS)
     if constexpr (kMcOk<BM> &&
                   (BM * BN <= 256 * 128 || (DORA_MC_DIRECT && BM >= 128 && BN >= 128)))
-      if (!akc && !bkc) return launch_bf16<BM, BN, WM, WN, false, false>(a, epi, out_f32, grid, st);
+      if (!akc && !bkc) return launch_bf16<BM, BN, WM, WN, S, false, false>(a, epi, out_f32, grid, st);
   }
   return hipErrorInvalidValue;
 }
@@ -1073,15 +1114,16 @@ hipError_t launch_layout(bool akc, bool bkc, const KArgs& a, int epi, bool out_f
 hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool out_f32, dim3 grid,
                       hipStream_t st) {
   switch (cfg) {
-    case 0: return launch_layout<256, 256, 2, 4>(akc, bkc, a, epi, out_f32, grid, st);
-    case 1: return launch_layout<256, 128, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 2: return launch_layout<128, 128, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 3: return launch_layout<128, 256, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 4: return launch_layout<64, 64, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 5: return launch_layout<256, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 6: return launch_layout<128, 384, 2, 4>(akc, bkc, a, epi, out_f32, grid, st);
-    case 7: return launch_layout<384, 128, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 8: return launch_layout<128, 192, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 0: return launch_layout<256, 256, 2, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 1: return launch_layout<256, 128, 2, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 2: return launch_layout<128, 128, 2, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 3: return launch_layout<128, 256, 2, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 4: return launch_layout<64, 64, 2, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 5: return launch_layout<256, 128, 4, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 6: return launch_layout<128, 384, 2, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 7: return launch_layout<384, 128, 4, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 8: return launch_layout<128, 192, 2, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
+    case 9: return launch_layout<128, 128, 2, 2, 3>(akc, bkc, a, epi, out_f32, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1170,15 +1212,34 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bk
   const bool both_mc = !akc && !bkc;
   if ((DORA_MC_DIRECT || !both_mc) && tiles(0) >= 256) return {0, 1};
   if (tiles(5) >= 256) return {5, 1};   // only when it still fills every CU
-  // Skinny or small, split along K: 128 x 128 tiles at ~384 workgroups did best
-  // for every operand layout of the d = 8192, r = 384 layer (xs, P, ts, dB, dA).
-  const int cfg = 2;
-  const int64_t target = 384;
-  const int64_t t = tiles(cfg);
-  int64_t split = (target + t / 2) / t;
-  split = std::min<int64_t>(split, std::max<int64_t>(1, ktiles / 8));
-  split = std::max<int64_t>(1, std::min<int64_t>(split, 16));
-  return {cfg, (int)split};
+  // Skinny or small: 128 x 128 tiles, split along K into as many parts as one
+  // round of workgroups holds (throughput grows with the workgroups resident
+  // at once).  Two-stage tiles take two workgroups per CU (512 slots), the
+  // three-stage ones one (256 slots); the plan whose round is fuller wins, and
+  // a tie goes to fewer splits (less partial-sum traffic; one split needs no
+  // reduction).  Measured on the d = 8192, r = 384 layer: x A^T and g_z B take
+  // two stages and 5 splits, dB and dA three stages and no split.
+  struct Cand {
+    int cfg;
+    int64_t slots;
+  };
+  const Cand cands[2] = {{2, 512}, {9, 256}};
+  GemmPlan best = {2, 1};
+  int64_t best_wgs = 0, best_cap = 1;   // fill = best_wgs / best_cap
+  for (const Cand& c : cands) {
+    const int64_t t = tiles(c.cfg);
+    int64_t split = std::max<int64_t>(1, c.slots / t);
+    split = std::min<int64_t>(split, std::max<int64_t>(1, ktiles / 8));
+    split = std::min<int64_t>(split, 16);
+    const int64_t wgs = t * split, cap = cdiv64(wgs, c.slots) * c.slots;
+    if (best_wgs == 0 || wgs * best_cap > best_wgs * cap ||
+        (wgs * best_cap == best_wgs * cap && split < best.split)) {
+      best = {c.cfg, (int)split};
+      best_wgs = wgs;
+      best_cap = cap;
+    }
+  }
+  return best;
 }
 
 GemmPlan plan_norm_projection(int64_t M, int64_t N, int64_t K, int64_t ld_max) {
