@@ -101,7 +101,7 @@ struct Layout {
   size_t rowsq = 0, rowdot = 0;                  // norm: the projection's per-row partials
   int64_t dot_parts = 0;
   size_t xs = 0, slora = 0;                      // forward
-  size_t gz = 0, ts = 0, dmpart = 0;             // backward
+  size_t gz = 0, ts = 0, dmpart = 0, bg = 0;     // backward
   size_t mnorm = 0;                              // merge: the row norms when not given
   size_t vpart = 0;                              // DVoRA: row-block partials of grad_d
   // backward with the undetached norm gradient
@@ -109,7 +109,7 @@ struct Layout {
          hlo = 0, d1 = 0;
   int qsplits = 1, hsplits = 1, d1splits = 1;
   size_t scratch = 0, scratch_bytes = 0;         // split-K partial sums
-  size_t scratch2 = 0, scratch2_bytes = 0;       // backward: dB's partials on the side stream
+  size_t scratch2 = 0, scratch2_bytes = 0;       // backward: ts's split-K on the side stream
   size_t total = 0;
   int splits = 1, psplits = 1;
   int64_t dm_blocks = 0;
@@ -169,6 +169,7 @@ Layout layout(const dora_shape& s, int op) {
     L.xs = take(T * r * e);
     L.gz = take(T * (size_t)s.d_out * e);
     L.ts = take(T * r * e);
+    L.bg = take((size_t)s.d_out * r * e);
     L.dm_blocks = cdiv(s.tokens, kTokPerDmBlock);
     L.dmpart = take((size_t)L.dm_blocks * s.d_out * 4);
     need(s.tokens, s.r, s.d_in);                         // xs recomputed
@@ -176,7 +177,8 @@ Layout layout(const dora_shape& s, int op) {
     need(s.tokens, s.d_in, s.d_out + s.r, true, false);  // dx
     need(s.d_out, s.r, s.tokens, false, false);          // dB
     need(s.r, s.d_in, s.tokens, false, false);           // dA
-    L.scratch2_bytes = gemm_scratch_bytes(s.d_out, s.r, s.tokens, dt, false, false);
+    // ts on the side stream, beside the compose backward
+    L.scratch2_bytes = gemm_scratch_bytes(s.tokens, s.r, s.d_out, dt, true, false);
     L.scratch2 = take(L.scratch2_bytes);
     if ((s.flags & DORA_FLAG_EXACT_NORM_GRAD) && s.r > 0) {
       L.dm = take((size_t)s.d_out * 4);
@@ -324,7 +326,7 @@ void give_scratch(GemmProblem& g, void* ws, const Layout& L) {
   g.scratch_bytes = L.scratch_bytes;
 }
 
-// The backward's second split-K region, for dB while ts runs beside it.
+// The backward's second split-K region, for ts on the side stream.
 void give_scratch2(GemmProblem& g, void* ws, const Layout& L) {
   g.scratch = L.scratch2_bytes ? at(ws, L.scratch2) : nullptr;
   g.scratch_bytes = L.scratch2_bytes;
@@ -573,20 +575,35 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
   // Undetached norm (DoRA reading notes, Appendix A.1): only A and B see it.
   const bool exact = (s.flags & DORA_FLAG_EXACT_NORM_GRAD) && has_r && (grad_A || grad_B);
 
-  // gz = g * gy and the dm partial sums.
+  // gz = g * gy (for dx and dB) and the dm partial sums; ts = s (gz B) is
+  // formed as gy Bg with Bg = s diag(g) B, from the incoming gradient alone.
   void* gz = at(ws, L.gz);
   float* dmpart = reinterpret_cast<float*>(at(ws, L.dmpart));
-  const bool need_gz = (grad_x && !noT) || (has_r && (grad_A || grad_B));
+  const bool need_gz = (grad_x && !noT) || (has_r && grad_B);
+  const bool need_ts = has_r && !noT && (grad_x || grad_A);
   float* kappa = nullptr;   // A.1: k' and Q (set below when the norm is undetached)
   float* q = nullptr;
   float* dm = grad_m ? grad_m : (exact ? reinterpret_cast<float*>(at(ws, L.dm)) : nullptr);
-  if (need_gz || dm)
-    HIP_TRY(compose_bwd(grad_y, y, m, norm, gz, dmpart, s.tokens, s.d_out, kTokPerDmBlock, dt, st));
-  // With the norm detached, dm and dB = gz^T xs depend only on compose_bwd's
-  // outputs (and the saved xs): they run on a side stream (dB with its own
-  // split-K region) beside ts, and join before the call returns.
-  SideStream* side = (!exact && has_r && grad_B && xs && !noT) ? side_stream() : nullptr;
-  auto grad_b = [&](hipStream_t on, bool second_scratch, const void* xsu) -> int {
+  void* ts = at(ws, L.ts);
+  auto t_proj = [&](hipStream_t on, bool second_scratch) -> int {
+    void* bg = at(ws, L.bg);
+    HIP_TRY(scale_b_rows(B, m, norm, s.s, bg, s.d_out, s.r, dt, on));
+    GemmProblem t;
+    t.M = s.tokens;
+    t.N = s.r;
+    t.nseg = 1;
+    t.seg[0] = {grad_y, bg, s.d_out, s.r, s.d_out};
+    t.b_kcontig = false;
+    t.c = ts;
+    t.ldc = s.r;
+    if (second_scratch)
+      give_scratch2(t, ws, L);
+    else
+      give_scratch(t, ws, L);
+    HIP_TRY(gemm(t, dt, on, "t_proj"));
+    return DORA_OK;
+  };
+  auto grad_b = [&](const void* xsu) -> int {
     GemmProblem b;
     b.M = s.d_out;
     b.N = s.r;
@@ -596,38 +613,61 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     b.b_kcontig = false;
     b.c = grad_B;
     b.ldc = s.r;
-    if (second_scratch)
-      give_scratch2(b, ws, L);
-    else
-      give_scratch(b, ws, L);
+    give_scratch(b, ws, L);
     if (exact) {   // float32 partial sums, combined with diag(k') Q in one rounding
       float* d1 = reinterpret_cast<float*>(at(ws, L.d1));
       b.c = d1;
       b.out_f32 = true;
       b.split = L.d1splits;
       b.split_stride = s.d_out * s.r;
-      HIP_TRY(gemm(b, dt, on, "dB_gemm"));
-      HIP_TRY(db_combine(d1, L.d1splits, q, L.qsplits, kappa, grad_B, s.d_out, s.r, dt, on));
+      HIP_TRY(gemm(b, dt, st, "dB_gemm"));
+      HIP_TRY(db_combine(d1, L.d1splits, q, L.qsplits, kappa, grad_B, s.d_out, s.r, dt, st));
     } else {
-      HIP_TRY(gemm(b, dt, on, "dB_gemm"));
+      HIP_TRY(gemm(b, dt, st, "dB_gemm"));
     }
+    return DORA_OK;
+  };
+  void* bk = nullptr;     // A.1: Bk' and H' (set below when the norm is undetached)
+  void* hmat = nullptr;
+  auto grad_a = [&]() -> int {
+    GemmProblem a;
+    a.M = s.r;
+    a.N = s.d_in;
+    a.nseg = 1;
+    a.seg[0] = {ts, x, s.r, s.d_in, s.tokens};
+    if (exact) {   // [ts^T | Bk'^T | H'] [x ; W0 ; A]  (H' is symmetric)
+      a.seg[1] = {bk, W0, s.r, s.d_in, s.d_out};
+      a.seg[2] = {hmat, A, s.r, s.d_in, s.r};
+      a.nseg = 3;
+    }
+    a.a_kcontig = false;
+    a.b_kcontig = false;
+    a.c = grad_A;
+    a.ldc = s.d_in;
+    give_scratch(a, ws, L);
+    HIP_TRY(gemm(a, dt, st, "dA_gemm"));
     return DORA_OK;
   };
   // columns with m_i == 0 take dm from its definition (y / m = z / n fails there)
   const DmRecompute zr{norm, grad_y, x, W0, A, B, s.s, s.tokens, s.d_in, s.r};
+
+  // With the norm detached, ts runs on the side stream beside the compose
+  // backward (one HBM-bound, the other latency-bound); dx waits for both.  The
+  // rest follows dx on the caller's stream: dx fills the chip in whole rounds
+  // of workgroups, and anything beside it only delays its second round.
+  SideStream* side = (!exact && need_ts) ? side_stream() : nullptr;
   SideFork fk(side, st);
   if (side) {
     HIP_TRY(fk.fork());
-    if (dm) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, zr, dt, fk.side()));
-    DORA_CHECK(grad_b(fk.side(), true, xs));
-  } else if (dm) {
-    HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, zr, dt, st));
+    DORA_CHECK(t_proj(fk.side(), true));
   }
+  if (need_gz || dm)
+    HIP_TRY(compose_bwd(grad_y, y, m, norm, gz, dmpart, s.tokens, s.d_out, kTokPerDmBlock, dt, st));
+  HIP_TRY(fk.join());   // dx below needs ts
+  if (dm) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, zr, dt, st));
 
   // A.1 terms: k' = -s m dm / n^2, Bk' = diag(k') B, Q = W0 A^T + s B G,
   // H' = s Bk'^T B.  Then dB += diag(k') Q and dA += Bk'^T W0 + H' A.
-  void* bk = nullptr;
-  void* hmat = nullptr;
   if (exact) {
     kappa = reinterpret_cast<float*>(at(ws, L.kappa));
     bk = at(ws, L.bk);
@@ -684,21 +724,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     }
   }
 
-  // ts = s (gz B), needed by grad_x and grad_A.
-  void* ts = at(ws, L.ts);
-  if (has_r && !noT && (grad_x || grad_A)) {
-    GemmProblem t;
-    t.M = s.tokens;
-    t.N = s.r;
-    t.nseg = 1;
-    t.seg[0] = {gz, B, s.d_out, s.r, s.d_out};
-    t.b_kcontig = false;
-    t.alpha = s.s;
-    t.c = ts;
-    t.ldc = s.r;
-    give_scratch(t, ws, L);
-    HIP_TRY(gemm(t, dt, st, "t_proj"));
-  }
+  if (!side && need_ts) DORA_CHECK(t_proj(st, false));
 
   if (grad_x && !noT) {
     GemmProblem d;
@@ -714,7 +740,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     HIP_TRY(gemm(d, dt, st, "dx_gemm"));
   }
 
-  if (grad_B && has_r && !side) {
+  if (grad_B && has_r) {
     const void* xsu = xs;
     if (!xsu && !noT) {
       void* xw = at(ws, L.xs);
@@ -730,27 +756,10 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
       HIP_TRY(gemm(d, dt, st, "down_proj_xs"));
       xsu = xw;
     }
-    DORA_CHECK(grad_b(st, false, xsu));
+    DORA_CHECK(grad_b(xsu));
   }
 
-  if (grad_A && has_r) {
-    GemmProblem a;
-    a.M = s.r;
-    a.N = s.d_in;
-    a.nseg = 1;
-    a.seg[0] = {ts, x, s.r, s.d_in, s.tokens};
-    if (exact) {   // [ts^T | Bk'^T | H'] [x ; W0 ; A]  (H' is symmetric)
-      a.seg[1] = {bk, W0, s.r, s.d_in, s.d_out};
-      a.seg[2] = {hmat, A, s.r, s.d_in, s.r};
-      a.nseg = 3;
-    }
-    a.a_kcontig = false;
-    a.b_kcontig = false;
-    a.c = grad_A;
-    a.ldc = s.d_in;
-    give_scratch(a, ws, L);
-    HIP_TRY(gemm(a, dt, st, "dA_gemm"));
-  }
+  if (grad_A && has_r) DORA_CHECK(grad_a());
   HIP_TRY(fk.join());
   return DORA_OK;
 }

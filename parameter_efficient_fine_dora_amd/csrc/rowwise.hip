@@ -356,6 +356,25 @@ __global__ __launch_bounds__(256) void dora_exact_prep(const void* m, const floa
   }
 }
 
+// Bg = s diag(g) B with g_i = m_i / max(n_i, eps) (float32 product, rounded
+// once): with it the rank-space gradient ts = s (g * gy) B is gy Bg, which
+// needs only the incoming gradient and so need not wait for the compose
+// backward.
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_scale_b_rows(const void* B, const void* m,
+                                                         const float* norm, float s, void* Bg,
+                                                         int64_t n, int64_t r) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const int64_t i = idx / r;
+  const float g = Vec<BF>::scalar(m, i) / fmaxf(norm[i], kNormEps);
+  const float v = s * g * Vec<BF>::scalar(B, idx);
+  if (BF)
+    reinterpret_cast<uint16_t*>(Bg)[idx] = f32_to_bf16(v);
+  else
+    reinterpret_cast<float*>(Bg)[idx] = v;
+}
+
 // dB = sum_z D1_z + k'_i * sum_z Q_z, each in a fixed order, rounded once.
 template <bool BF>
 __global__ __launch_bounds__(256) void dora_db_combine(const float* d1, int d1_splits,
@@ -588,6 +607,19 @@ hipError_t compose_bwd(const void* gy, const void* y, const void* m, const float
   else
     hipLaunchKernelGGL(dora_compose_bwd<false>, grid, dim3(256), 0, st, gy, y, m, norm, gz,
                        dm_part, T, d_out, tokens_per_block);
+  return hipGetLastError();
+}
+
+hipError_t scale_b_rows(const void* B, const void* m, const float* norm, float s, void* Bg,
+                        int64_t d_out, int64_t r, int dtype, hipStream_t st) {
+  const int64_t n = d_out * r;
+  if (n <= 0) return hipSuccess;
+  LaunchTimer t("bg_scale", st);
+  const dim3 grid((unsigned)cdiv(n, 256));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dora_scale_b_rows<true>, grid, dim3(256), 0, st, B, m, norm, s, Bg, n, r);
+  else
+    hipLaunchKernelGGL(dora_scale_b_rows<false>, grid, dim3(256), 0, st, B, m, norm, s, Bg, n, r);
   return hipGetLastError();
 }
 

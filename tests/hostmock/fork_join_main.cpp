@@ -61,6 +61,43 @@ static bool check(const char* what, int rc, hipStream_t caller) {
   return true;
 }
 
+// Whether every launch labelled `consumer` is ordered after every launch
+// labelled `producer` (same stream and later, or reached through recorded
+// events); true when either label is absent (a failed call stops early).
+static bool ordered_after(const char* consumer, const char* producer) {
+  const auto& log = mock::log();
+  struct Clock { std::map<MockStream*, long> seen; long launches = 0; };
+  struct Launch { MockStream* stream; long index; std::map<MockStream*, long> seen; };
+  std::map<MockStream*, Clock> clk;
+  std::map<long, std::map<MockStream*, long>> snap;
+  std::vector<Launch> prod, cons;
+  for (const Op& o : log) {
+    Clock& c = clk[o.stream];
+    if (o.kind == Op::kLaunch) {
+      Launch l{o.stream, c.launches, c.seen};
+      if (o.label == producer) prod.push_back(l);
+      if (o.label == consumer) cons.push_back(l);
+      ++c.launches;
+    } else if (o.kind == Op::kRecord) {
+      auto s = c.seen;
+      s[o.stream] = c.launches;
+      snap[o.stamp] = s;
+    } else {
+      for (auto& kv : snap[o.stamp]) c.seen[kv.first] = std::max(c.seen[kv.first], kv.second);
+    }
+  }
+  for (const Launch& q : cons)
+    for (const Launch& p : prod) {
+      const bool ok = q.stream == p.stream ? p.index < q.index
+                                           : (q.seen.count(p.stream) && q.seen.at(p.stream) > p.index);
+      if (!ok) {
+        std::printf("%s is not ordered after %s\n", consumer, producer);
+        return false;
+      }
+    }
+  return true;
+}
+
 int main() {
   MockStream caller_obj{100};
   hipStream_t caller = &caller_obj;
@@ -72,11 +109,21 @@ int main() {
   int rc = dora_forward(&s, fake, fake, fake, fake, fake, fake, reinterpret_cast<float*>(fake),
                         fake, fake, dora_workspace_bytes(&s, DORA_OP_FORWARD), caller);
   ok &= check("forward", rc, caller);
+  ok &= ordered_after("fused_fwd_gemm", "down_proj_xs");
+  ok &= ordered_after("fused_fwd_gemm", "norm_finalize");
+  ok &= ordered_after("norm_finalize", "cross_gram_proj");
+  ok &= ordered_after("cross_gram_proj", "gram_finalize");
 
   mock::log().clear();
   rc = dora_backward(&s, fake, fake, fake, fake, fake, fake, reinterpret_cast<float*>(fake), fake,
                      fake, fake, fake, fake, reinterpret_cast<float*>(fake), fake,
                      dora_workspace_bytes(&s, DORA_OP_BACKWARD), caller);
   ok &= check("backward", rc, caller);
+  ok &= ordered_after("t_proj", "bg_scale");
+  ok &= ordered_after("dx_gemm", "t_proj");
+  ok &= ordered_after("dx_gemm", "compose_bwd");
+  ok &= ordered_after("dA_gemm", "t_proj");
+  ok &= ordered_after("dm_finalize", "compose_bwd");
+  ok &= ordered_after("dB_gemm", "compose_bwd");
   return ok ? 0 : 1;
 }

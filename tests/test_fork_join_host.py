@@ -1,7 +1,8 @@
 """The C ABI's fork/join on its side stream, on the host: csrc/api.hip is built
 with g++ against a stand-in HIP runtime (tests/hostmock) whose kernel launchers
 can be made to fail one by one.  Whatever launch fails, the call must leave the
-caller's stream ordered after all side-stream work and no fork open."""
+caller's stream ordered after all side-stream work and no fork open; on the
+normal path every kernel is ordered after the kernels whose outputs it reads."""
 from __future__ import annotations
 
 import os
@@ -16,8 +17,8 @@ CSRC = os.path.join(ROOT, "parameter_efficient_fine_dora_amd", "csrc")
 
 # every launch label of the forward and the detached backward
 LABELS = ["", "down_proj_xs", "gram_AAt", "gram_finalize", "cross_gram_proj", "norm_finalize",
-          "fused_fwd_gemm", "compose_bwd", "dm_finalize", "dB_gemm", "t_proj", "dx_gemm",
-          "dA_gemm"]
+          "fused_fwd_gemm", "compose_bwd", "dm_finalize", "dB_gemm", "bg_scale", "t_proj",
+          "dx_gemm", "dA_gemm"]
 
 
 @pytest.fixture(scope="module")
