@@ -359,20 +359,31 @@ __global__ __launch_bounds__(256) void dora_exact_prep(const void* m, const floa
 // Bg = s diag(g) B with g_i = m_i / max(n_i, eps) (float32 product, rounded
 // once): with it the rank-space gradient ts = s (g * gy) B is gy Bg, which
 // needs only the incoming gradient and so need not wait for the compose
-// backward.
-template <bool BF>
+// backward.  One 16-byte vector per thread when r is a multiple of the vector
+// width (a vector then lies in one row), else one element.
+template <bool BF, bool VEC>
 __global__ __launch_bounds__(256) void dora_scale_b_rows(const void* B, const void* m,
                                                          const float* norm, float s, void* Bg,
                                                          int64_t n, int64_t r) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  using V = Vec<BF>;
+  constexpr int kW = VEC ? V::kN : 1;
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kW;
   if (idx >= n) return;
   const int64_t i = idx / r;
-  const float g = Vec<BF>::scalar(m, i) / fmaxf(norm[i], kNormEps);
-  const float v = s * g * Vec<BF>::scalar(B, idx);
-  if (BF)
-    reinterpret_cast<uint16_t*>(Bg)[idx] = f32_to_bf16(v);
-  else
-    reinterpret_cast<float*>(Bg)[idx] = v;
+  const float sg = s * (V::scalar(m, i) / fmaxf(norm[i], kNormEps));
+  if constexpr (VEC) {
+    float v[V::kN];
+    V::load(B, idx / V::kN, v);
+#pragma unroll
+    for (int q = 0; q < V::kN; ++q) v[q] *= sg;
+    V::store(Bg, idx / V::kN, v);
+  } else {
+    const float v = sg * V::scalar(B, idx);
+    if (BF)
+      reinterpret_cast<uint16_t*>(Bg)[idx] = f32_to_bf16(v);
+    else
+      reinterpret_cast<float*>(Bg)[idx] = v;
+  }
 }
 
 // dB = sum_z D1_z + k'_i * sum_z Q_z, each in a fixed order, rounded once.
@@ -615,11 +626,24 @@ hipError_t scale_b_rows(const void* B, const void* m, const float* norm, float s
   const int64_t n = d_out * r;
   if (n <= 0) return hipSuccess;
   LaunchTimer t("bg_scale", st);
-  const dim3 grid((unsigned)cdiv(n, 256));
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(dora_scale_b_rows<true>, grid, dim3(256), 0, st, B, m, norm, s, Bg, n, r);
-  else
-    hipLaunchKernelGGL(dora_scale_b_rows<false>, grid, dim3(256), 0, st, B, m, norm, s, Bg, n, r);
+  const int64_t w = dtype == kBF16 ? 8 : 4;
+  const bool vec = r % w == 0;
+  const dim3 grid((unsigned)cdiv(vec ? n / w : n, 256));
+  if (dtype == kBF16) {
+    if (vec)
+      hipLaunchKernelGGL((dora_scale_b_rows<true, true>), grid, dim3(256), 0, st, B, m, norm, s, Bg,
+                         n, r);
+    else
+      hipLaunchKernelGGL((dora_scale_b_rows<true, false>), grid, dim3(256), 0, st, B, m, norm, s,
+                         Bg, n, r);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((dora_scale_b_rows<false, true>), grid, dim3(256), 0, st, B, m, norm, s,
+                         Bg, n, r);
+    else
+      hipLaunchKernelGGL((dora_scale_b_rows<false, false>), grid, dim3(256), 0, st, B, m, norm, s,
+                         Bg, n, r);
+  }
   return hipGetLastError();
 }
 
