@@ -6,9 +6,9 @@ record count; the scalar offset is added after the check.  So every row a load
 reaches must be reachable through the per-lane offset alone: a load whose
 per-lane offset passes the check must stay inside the operand once the scalar
 offset is added, and a load for a row past the operand must fail the check.
-The replay mirrors prepare() / issue_rows() of CopyKC, including the kOne path
-of the eight-wave tiles (one per-lane offset for every instruction, the row step
-in the scalar offset on full tiles only).
+The replay mirrors prepare() / issue() of CopyKC: every copy instruction has its
+own per-lane offset (its row and chunk), and a step adds only the K position
+as the scalar offset.
 """
 from __future__ import annotations
 
@@ -25,34 +25,30 @@ def swz(row):
     return (row & 7) ^ ((row >> 3) & 7)
 
 
-def copy_loads(R, NW, ld, rows, K, kt, rowstep_always_in_soff=False):
-    """Yield (row, chunk, voffset, soffset, records) for every lane load of step kt."""
+def copy_loads(R, NW, ld, rows, K, kt, rowstep_in_soff=False):
+    """Yield (row, chunk, voffset, soffset, records) for every lane load of step kt.
+
+    rowstep_in_soff replays a wrong variant (one per-lane offset for every
+    instruction, the row step added through the scalar offset)."""
     n_instr = R // 8 // NW
-    k_one = NW % 8 == 0
-    full = rows == R
     records = min(rows * ld * 2, 0x7FFFFFFF)
     step = NW * 8 * ld * 2
     kbytes = kt * ROW_BYTES
     tail = (K % KBK) != 0 and kt == (K + KBK - 1) // KBK - 1
     for wave, lane in itertools.product(range(NW), range(64)):
-        row0 = (wave + 0 * NW) * 8 + (lane >> 3)
-        off = []
-        for i in range(1 if k_one else n_instr):
-            row = (wave + i * NW) * 8 + (lane >> 3)
-            kc = (lane & 7) ^ swz(row)
-            off.append(row * ld * 2 + kc * 16)
-        in_soff = k_one and (full or rowstep_always_in_soff)
         for i in range(n_instr):
             row = (wave + i * NW) * 8 + (lane >> 3)
             kc = (lane & 7) ^ swz(row)
-            if k_one:
-                o = off[0] if in_soff else off[0] + i * step
+            if rowstep_in_soff:
+                row0 = wave * 8 + (lane >> 3)
+                o = row0 * ld * 2 + ((lane & 7) ^ swz(row0)) * 16
+                kc = (lane & 7) ^ swz(row0)
+                soff = kbytes + i * step
             else:
-                o = off[i]
+                o = (row * ld * 2 + kc * 16) & 0xFFFFFFFF
+                soff = kbytes
             if tail and kt * KBK + kc * 8 >= K:
                 o = OOB
-            soff = kbytes + (i * step if in_soff else 0)
-            assert row0 + 8 * NW * i == row
             yield row, kc, o, soff, records
 
 
@@ -66,10 +62,11 @@ def violations(R, NW, ld, rows, K, **kw):
             byte = o + soff
             if row >= rows or byte >= rows * ld * 2:
                 bad.append((kt, row, kc, o, soff))
+                continue
             # inside the operand the load reads its own row's chunk at k < K
             k = kt * KBK + kc * 8
             assert byte == row * ld * 2 + k * 2, (row, kc, o, soff)
-            assert k < K or byte >= rows * ld * 2
+            assert k < K
     return bad
 
 
@@ -93,8 +90,16 @@ def test_every_checked_load_stays_inside_the_operand(R, NW, ld, rows, K):
 
 
 def test_row_step_in_the_scalar_offset_reads_past_a_ragged_tile():
-    """The arithmetic the copy used before (row step always in the scalar offset on
-    eight-wave tiles) reads rows past the operand on a ragged tile; the replay sees it."""
-    bad = violations(256, 8, 512, 5, 512, rowstep_always_in_soff=True)
+    """A copy that puts the row step into the scalar offset reads rows past the
+    operand on a ragged tile; the replay sees it (and nothing on a full tile)."""
+    bad = violations(256, 8, 512, 5, 512, rowstep_in_soff=True)
     assert bad and max(b[1] for b in bad) >= 64
-    assert violations(256, 8, 512, 256, 512, rowstep_always_in_soff=True) == []
+    assert violations(256, 8, 512, 256, 512, rowstep_in_soff=True) == []
+
+
+def test_per_lane_offsets_fit_32_bits_on_the_widest_tiles():
+    """Per-lane offsets reach (R - 1) * ld * 2 + 112; the planner keeps R * ld * 2
+    below 2^31, which for 384-row tiles allows strides up to 2^21 elements."""
+    for R, ld in ((256, (1 << 22) - 8), (384, (1 << 21) - 8)):
+        assert R * ld * 2 < (1 << 31)
+        assert (R - 1) * ld * 2 + 7 * 16 < (1 << 32)
