@@ -173,12 +173,12 @@ Layout layout(const dora_shape& s, int op) {
     L.dm_blocks = cdiv(s.tokens, kTokPerDmBlock);
     L.dmpart = take((size_t)L.dm_blocks * s.d_out * 4);
     need(s.tokens, s.r, s.d_in);                         // xs recomputed
-    need(s.tokens, s.r, s.d_out, true, false);           // ts = s gz B
+    need(s.tokens, s.r, s.d_out);                        // ts = gy Bg
     need(s.tokens, s.d_in, s.d_out + s.r, true, false);  // dx
     need(s.d_out, s.r, s.tokens, false, false);          // dB
     need(s.r, s.d_in, s.tokens, false, false);           // dA
     // ts on the side stream, beside the compose backward
-    L.scratch2_bytes = gemm_scratch_bytes(s.tokens, s.r, s.d_out, dt, true, false);
+    L.scratch2_bytes = gemm_scratch_bytes(s.tokens, s.r, s.d_out, dt, true, true);
     L.scratch2 = take(L.scratch2_bytes);
     if ((s.flags & DORA_FLAG_EXACT_NORM_GRAD) && s.r > 0) {
       L.dm = take((size_t)s.d_out * 4);
@@ -576,7 +576,8 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
   const bool exact = (s.flags & DORA_FLAG_EXACT_NORM_GRAD) && has_r && (grad_A || grad_B);
 
   // gz = g * gy (for dx and dB) and the dm partial sums; ts = s (gz B) is
-  // formed as gy Bg with Bg = s diag(g) B, from the incoming gradient alone.
+  // formed as gy Bg with Bg = s diag(g) B (stored transposed, so both operands
+  // are K-contiguous), from the incoming gradient alone.
   void* gz = at(ws, L.gz);
   float* dmpart = reinterpret_cast<float*>(at(ws, L.dmpart));
   const bool need_gz = (grad_x && !noT) || (has_r && grad_B);
@@ -586,14 +587,13 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
   float* dm = grad_m ? grad_m : (exact ? reinterpret_cast<float*>(at(ws, L.dm)) : nullptr);
   void* ts = at(ws, L.ts);
   auto t_proj = [&](hipStream_t on, bool second_scratch) -> int {
-    void* bg = at(ws, L.bg);
-    HIP_TRY(scale_b_rows(B, m, norm, s.s, bg, s.d_out, s.r, dt, on));
+    void* bgt = at(ws, L.bg);   // (s diag(g) B)^T, [r, d_out]
+    HIP_TRY(scale_b_rows_t(B, m, norm, s.s, bgt, s.d_out, s.r, dt, on));
     GemmProblem t;
     t.M = s.tokens;
     t.N = s.r;
     t.nseg = 1;
-    t.seg[0] = {grad_y, bg, s.d_out, s.r, s.d_out};
-    t.b_kcontig = false;
+    t.seg[0] = {grad_y, bgt, s.d_out, s.d_out, s.d_out};
     t.c = ts;
     t.ldc = s.r;
     if (second_scratch)

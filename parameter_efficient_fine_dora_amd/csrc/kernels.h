@@ -138,9 +138,9 @@ hipError_t compose_bwd(const void* gy, const void* y, const void* m, const float
                        float* dm_part, int64_t T, int64_t d_out, int64_t tokens_per_block,
                        int dtype, hipStream_t st);
 
-// Bg = s diag(g) B, g_i = m_i / max(n_i, eps), in the layer dtype.
-hipError_t scale_b_rows(const void* B, const void* m, const float* norm, float s, void* Bg,
-                        int64_t d_out, int64_t r, int dtype, hipStream_t st);
+// Bg^T = (s diag(g) B)^T, [r, d_out], g_i = m_i / max(n_i, eps), in the layer dtype.
+hipError_t scale_b_rows_t(const void* B, const void* m, const float* norm, float s, void* Bgt,
+                          int64_t d_out, int64_t r, int dtype, hipStream_t st);
 
 // What dm_finalize needs to recompute a column whose m_i is zero (where
 // y / m = z / n does not hold): dm_i = sum_t gy[t,i] (x_t . (W0_i + s B_i A)) / n_i.

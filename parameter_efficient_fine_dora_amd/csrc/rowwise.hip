@@ -356,33 +356,48 @@ __global__ __launch_bounds__(256) void dora_exact_prep(const void* m, const floa
   }
 }
 
-// Bg = s diag(g) B with g_i = m_i / max(n_i, eps) (float32 product, rounded
-// once): with it the rank-space gradient ts = s (g * gy) B is gy Bg, which
-// needs only the incoming gradient and so need not wait for the compose
-// backward.  One 16-byte vector per thread when r is a multiple of the vector
-// width (a vector then lies in one row), else one element.
-template <bool BF, bool VEC>
-__global__ __launch_bounds__(256) void dora_scale_b_rows(const void* B, const void* m,
-                                                         const float* norm, float s, void* Bg,
-                                                         int64_t n, int64_t r) {
+// Bg^T = (s diag(g) B)^T, [r, d_out], with g_i = m_i / max(n_i, eps) (float32
+// product, rounded once): with it the rank-space gradient ts = s (g * gy) B is
+// gy Bg, which needs only the incoming gradient (so it need not wait for the
+// compose backward), and with Bg stored transposed both operands of that
+// product are K-contiguous.  A workgroup moves one 64 x 64 block through LDS:
+// rows of B read along r, rows of Bg^T written along d_out, both coalesced.
+constexpr int kTb = 64;
+template <bool BF>
+__global__ __launch_bounds__(256) void dora_scale_b_rows_t(const void* B, const void* m,
+                                                           const float* norm, float s, void* Bgt,
+                                                           int64_t d_out, int64_t r) {
   using V = Vec<BF>;
-  constexpr int kW = VEC ? V::kN : 1;
-  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kW;
-  if (idx >= n) return;
-  const int64_t i = idx / r;
-  const float sg = s * (V::scalar(m, i) / fmaxf(norm[i], kNormEps));
-  if constexpr (VEC) {
-    float v[V::kN];
-    V::load(B, idx / V::kN, v);
+  constexpr int kC = kTb / V::kN;   // 16-byte chunks along one 64-wide row of the block
+  __shared__ float tile[kTb][kTb + 1];
+  __shared__ float sg[kTb];
+  const int64_t i0 = (int64_t)blockIdx.x * kTb, q0 = (int64_t)blockIdx.y * kTb;
+  if (threadIdx.x < kTb) {
+    const int64_t i = i0 + threadIdx.x;
+    sg[threadIdx.x] = i < d_out ? s * (V::scalar(m, i) / fmaxf(norm[i], kNormEps)) : 0.f;
+  }
+  __syncthreads();
+  // d_out and r are multiples of the vector width, so a chunk is wholly inside or outside
+  for (int e = threadIdx.x; e < kTb * kC; e += 256) {
+    const int il = e / kC, ql = (e % kC) * V::kN;
+    const int64_t i = i0 + il, q = q0 + ql;
+    if (i < d_out && q < r) {
+      float v[V::kN];
+      V::load(B, (i * r + q) / V::kN, v);
 #pragma unroll
-    for (int q = 0; q < V::kN; ++q) v[q] *= sg;
-    V::store(Bg, idx / V::kN, v);
-  } else {
-    const float v = sg * V::scalar(B, idx);
-    if (BF)
-      reinterpret_cast<uint16_t*>(Bg)[idx] = f32_to_bf16(v);
-    else
-      reinterpret_cast<float*>(Bg)[idx] = v;
+      for (int u = 0; u < V::kN; ++u) tile[il][ql + u] = sg[il] * v[u];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < kTb * kC; e += 256) {
+    const int ql = e / kC, il = (e % kC) * V::kN;
+    const int64_t i = i0 + il, q = q0 + ql;
+    if (i < d_out && q < r) {
+      float v[V::kN];
+#pragma unroll
+      for (int u = 0; u < V::kN; ++u) v[u] = tile[il + u][ql];
+      V::store(Bgt, (q * d_out + i) / V::kN, v);
+    }
   }
 }
 
@@ -621,29 +636,17 @@ hipError_t compose_bwd(const void* gy, const void* y, const void* m, const float
   return hipGetLastError();
 }
 
-hipError_t scale_b_rows(const void* B, const void* m, const float* norm, float s, void* Bg,
-                        int64_t d_out, int64_t r, int dtype, hipStream_t st) {
-  const int64_t n = d_out * r;
-  if (n <= 0) return hipSuccess;
+hipError_t scale_b_rows_t(const void* B, const void* m, const float* norm, float s, void* Bgt,
+                          int64_t d_out, int64_t r, int dtype, hipStream_t st) {
+  if (d_out <= 0 || r <= 0) return hipSuccess;
   LaunchTimer t("bg_scale", st);
-  const int64_t w = dtype == kBF16 ? 8 : 4;
-  const bool vec = r % w == 0;
-  const dim3 grid((unsigned)cdiv(vec ? n / w : n, 256));
-  if (dtype == kBF16) {
-    if (vec)
-      hipLaunchKernelGGL((dora_scale_b_rows<true, true>), grid, dim3(256), 0, st, B, m, norm, s, Bg,
-                         n, r);
-    else
-      hipLaunchKernelGGL((dora_scale_b_rows<true, false>), grid, dim3(256), 0, st, B, m, norm, s,
-                         Bg, n, r);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((dora_scale_b_rows<false, true>), grid, dim3(256), 0, st, B, m, norm, s,
-                         Bg, n, r);
-    else
-      hipLaunchKernelGGL((dora_scale_b_rows<false, false>), grid, dim3(256), 0, st, B, m, norm, s,
-                         Bg, n, r);
-  }
+  const dim3 grid((unsigned)cdiv(d_out, kTb), (unsigned)cdiv(r, kTb));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dora_scale_b_rows_t<true>, grid, dim3(256), 0, st, B, m, norm, s, Bgt,
+                       d_out, r);
+  else
+    hipLaunchKernelGGL(dora_scale_b_rows_t<false>, grid, dim3(256), 0, st, B, m, norm, s, Bgt,
+                       d_out, r);
   return hipGetLastError();
 }
 

@@ -121,8 +121,8 @@ hipError_t compose_bwd(const void*, const void*, const void*, const float*, void
                        int64_t, int64_t, int, hipStream_t st) {
   return launch("compose_bwd", st);
 }
-hipError_t scale_b_rows(const void*, const void*, const float*, float, void*, int64_t, int64_t,
-                        int, hipStream_t st) {
+hipError_t scale_b_rows_t(const void*, const void*, const float*, float, void*, int64_t, int64_t,
+                          int, hipStream_t st) {
   return launch("bg_scale", st);
 }
 hipError_t dm_finalize(const float*, int64_t, const void*, float*, int64_t, const DmRecompute&, int,
