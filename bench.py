@@ -53,8 +53,8 @@ DEFAULT_CONFIG = "highrank_bwd_bf16"
 
 KERNEL_SOURCES = ["include/dora.h"] + [
     f"parameter_efficient_fine_dora_amd/csrc/{f}"
-    for f in ("api.hip", "gemm.hip", "gram.hip", "rowwise.hip", "noalloc.hip", "common.h",
-              "kernels.h", "entry.h")]
+    for f in ("api.hip", "gemm.hip", "gram.hip", "rowwise.hip", "small.hip", "noalloc.hip",
+              "common.h", "kernels.h", "entry.h")]
 WORKLOAD_TAG = "highrank_d8192_r384_t4096"
 
 
@@ -103,6 +103,11 @@ def algorithmic_work(d_out, d_in, r, T, e=2):
         "dB_gemm": ("flop", 2 * d_out * r * T),
         "dA_gemm": ("flop", 2 * r * d_in * T),
         "gram_finalize": ("byte", r * r * 4 * 2 + r * r * 4),
+        # a small float32 layer's forward: one pass over K (x W0^T, x A^T, W0 A^T,
+        # A A^T and ||W0_i||^2), then the split sums, the norm and the compose
+        "small_partials": ("flop", 2 * T * d_out * d_in + 2 * T * r * d_in + 2 * d_out * r * d_in
+                           + 2 * r * r * d_in + 2 * d_out * d_in),
+        "small_finish": ("flop", 2 * T * d_out * r + 2 * d_out * r * r + 4 * d_out * r),
     }
 
 
@@ -559,15 +564,18 @@ def main():
     if peaks and compose_fwd:
         compose_fwd["frac_measured_hbm"] = round(compose_fwd["gbps"] / peaks["hbm_stream_GBs"], 4)
     # the dominant kernel among those with a work model (split-K reductions have none)
-    dominant = max((k for k in timing if k in work), key=lambda k: timing[k][1])
-    kind, amount = work[dominant]
-    avg_s = timing[dominant][1] / timing[dominant][0] * 1e-3
-    if kind == "flop":
+    dominant = max((k for k in timing if k in work), key=lambda k: timing[k][1], default=None)
+    kind, amount = work[dominant] if dominant else (None, 0)
+    avg_s = timing[dominant][1] / timing[dominant][0] * 1e-3 if dominant else 0.0
+    if dominant is None:
+        roof = None
+    elif kind == "flop":
         achieved = amount / avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": flop_peak,
+        roof = {"bound": "mfma" if is_bf else "alu", "achieved": round(achieved, 2),
+                "peak": flop_peak,
                 "unit": "TFLOP/s", "frac": round(achieved / flop_peak, 4),
                 "traffic": traffic.get(dominant, {}).get("total_bytes"),
-                "kernel": dominant, "per_launch": f"{amount / 1e9:.1f} GFLOP",
+                "kernel": dominant, "per_launch": f"{amount / 1e9:.3g} GFLOP",
                 "avg_us": round(avg_s * 1e6, 2)}
         if peaks and is_bf:
             roof["frac_of_measured"] = round(achieved / peaks["mfma_bf16_TFs"], 4)

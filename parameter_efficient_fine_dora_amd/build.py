@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdora.so")
-SOURCES = ["api.hip", "gemm.hip", "gram.hip", "rowwise.hip", "probe.hip", "noalloc.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gram.hip", "rowwise.hip", "small.hip", "probe.hip", "noalloc.hip"]
 HEADERS = ["common.h", "kernels.h", "entry.h"]
 ARCH = "gfx950"
 

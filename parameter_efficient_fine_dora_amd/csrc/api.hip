@@ -83,6 +83,13 @@ int gram_splits(const dora_shape& s) {
 // (||W0_i||^2 from its pass over W0, B_i . P_i from its accumulators); P
 // itself is never stored.
 bool fused_norm(const dora_shape& s) { return s.dtype == kBF16 && s.r > 0; }
+// Small float32 layers run the whole forward (factored norm, xs and the
+// compose) in two kernels of their own, where the general path would be
+// launch latency throughout.
+bool small_path(const dora_shape& s) {
+  return s.dtype == kF32 && !(s.flags & DORA_FLAG_SEPARATE_COMPOSE) &&
+         small_forward_fits(s.tokens, s.d_out, s.d_in, s.r);
+}
 // bf16 projections use their own planner (one column tile where the rank fits);
 // float32 ones (and the undetached gradient's Q, which stores P) the generic one.
 GemmPlan p_plan(const dora_shape& s) {
@@ -101,6 +108,7 @@ struct Layout {
   size_t rowsq = 0, rowdot = 0;                  // norm: the projection's per-row partials
   int64_t dot_parts = 0;
   size_t xs = 0, slora = 0;                      // forward
+  size_t spart = 0;                              // forward of a small float32 layer: partials
   size_t gz = 0, ts = 0, dmpart = 0, bg = 0;     // backward
   size_t mnorm = 0;                              // merge: the row norms when not given
   size_t vpart = 0;                              // DVoRA: row-block partials of grad_d
@@ -126,6 +134,12 @@ Layout layout(const dora_shape& s, int op) {
     off += up(bytes);
     return o;
   };
+  if (op == DORA_OP_FORWARD && small_path(s)) {
+    L.xs = take(T * r * e);
+    L.spart = take(small_forward_plan(s.d_out, s.d_in).part_bytes);
+    L.total = off;
+    return L;
+  }
   size_t scratch = 0;
   auto need = [&](int64_t M, int64_t N, int64_t K, bool akc = true, bool bkc = true) {
     scratch = std::max(scratch, gemm_scratch_bytes(M, N, K, dt, akc, bkc));
@@ -472,11 +486,21 @@ int forward_impl(const dora_shape* shape, const void* x, const void* W0, const v
   const Layout L = layout(s, DORA_OP_FORWARD);
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   const int dt = s.dtype;
+  void* xs = xs_out ? xs_out : at(ws, L.xs);
+
+  if (small_path(s)) {
+    HIP_TRY(small_forward(reinterpret_cast<const float*>(x), reinterpret_cast<const float*>(W0),
+                          reinterpret_cast<const float*>(A), reinterpret_cast<const float*>(B),
+                          reinterpret_cast<const float*>(m), s.s, reinterpret_cast<float*>(y),
+                          norm_out, reinterpret_cast<float*>(xs),
+                          reinterpret_cast<float*>(at(ws, L.spart)), s.tokens, s.d_out, s.d_in,
+                          s.r, st));
+    return DORA_OK;
+  }
 
   // xs = s (x A^T): the down-projection, pre-scaled by s.  It does not depend
   // on the norm (and uses other workspace regions), so it runs on a side
   // stream beside the norm's chain and joins before the forward GEMM.
-  void* xs = xs_out ? xs_out : at(ws, L.xs);
   SideStream* side = (allow_side_stream && !noT && s.r > 0) ? side_stream() : nullptr;
   auto down_proj = [&](hipStream_t on) -> int {
     GemmProblem d;

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace dora {
 
 enum DType : int { kF32 = 0, kBF16 = 1 };
@@ -154,6 +156,41 @@ struct DmRecompute {
 // dm_i = sum_b dm_part[b, i] / m_i (fixed order); columns with m_i == 0 from `z`.
 hipError_t dm_finalize(const float* dm_part, int64_t blocks, const void* m, float* dm,
                        int64_t d_out, const DmRecompute& z, int dtype, hipStream_t st);
+
+// The whole forward of a small float32 layer in two kernels (csrc/small.hip):
+// norm, y and xs for tokens <= kSmallMaxTokens, r <= kSmallMaxRank,
+// d_in <= kSmallMaxDin, d_out <= kSmallMaxDout.  The first kernel splits K into
+// `ksplits` ranges of `chunks` 64-deep chunks over `row_blocks` blocks of 16
+// output rows and writes float32 partial sums to `part`; the second sums them
+// in split order and applies the norm and the compose.
+constexpr int kSmallMaxTokens = 64;
+constexpr int kSmallMaxRank = 32;
+constexpr int64_t kSmallMaxDin = 1024;
+constexpr int64_t kSmallMaxDout = 4096;
+struct SmallPlan {
+  int64_t row_blocks, ksplits, chunks;
+  size_t part_bytes;
+};
+inline bool small_forward_fits(int64_t T, int64_t d_out, int64_t d_in, int64_t r) {
+  return T >= 1 && T <= kSmallMaxTokens && r >= 0 && r <= kSmallMaxRank && d_in >= 1 &&
+         d_in <= kSmallMaxDin && d_out >= 1 && d_out <= kSmallMaxDout;
+}
+inline SmallPlan small_forward_plan(int64_t d_out, int64_t d_in) {
+  SmallPlan p;
+  p.row_blocks = (d_out + 15) / 16;
+  const int64_t nchunk = (d_in + 63) / 64;
+  // up to 256 workgroups where the row blocks alone leave the chip idle
+  const int64_t want = std::min<int64_t>(nchunk, std::max<int64_t>(1, 256 / p.row_blocks));
+  p.chunks = (nchunk + want - 1) / want;
+  p.ksplits = (nchunk + p.chunks - 1) / p.chunks;
+  // per (split, row block): z [64][16] and U | ||W0_i||^2 [16][33];
+  // per split: x A^T [64][32] and A A^T [32][32]
+  p.part_bytes = (size_t)p.ksplits * ((size_t)p.row_blocks * (64 * 16 + 16 * 33) + 64 * 32 + 32 * 32) * 4;
+  return p;
+}
+hipError_t small_forward(const float* x, const float* W0, const float* A, const float* B,
+                         const float* m, float s, float* y, float* norm, float* xs, float* part,
+                         int64_t T, int64_t d_out, int64_t d_in, int64_t r, hipStream_t st);
 
 // Launch bookkeeping for the optional per-kernel timing.
 struct LaunchTimer {

@@ -121,6 +121,12 @@ hipError_t compose_bwd(const void*, const void*, const void*, const float*, void
                        int64_t, int64_t, int, hipStream_t st) {
   return launch("compose_bwd", st);
 }
+hipError_t small_forward(const float*, const float*, const float*, const float*, const float*,
+                         float, float*, float*, float*, float*, int64_t, int64_t, int64_t, int64_t,
+                         hipStream_t st) {
+  const hipError_t e = launch("small_partials", st);
+  return e != hipSuccess ? e : launch("small_finish", st);
+}
 hipError_t scale_b_rows_t(const void*, const void*, const float*, float, void*, int64_t, int64_t,
                           int, hipStream_t st) {
   return launch("bg_scale", st);

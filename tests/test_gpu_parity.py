@@ -147,6 +147,10 @@ SMALL = [
     # r > d_in / 2 and K tails in every segment (d_in, r, d_out not multiples of 64)
     ("widerank_bf16", LayerShape(1032, 2056, 1016, 260, 2.0, "bf16"), 11, {}),
     ("widerank_f32", LayerShape(520, 776, 392, 70, 2.0, "f32"), 12, {}),
+    # float32 layers at the edge of the two-kernel small forward (64 tokens,
+    # rank 32, d_out and d_in just under their limits), and one token past it
+    ("smallmax_f32", LayerShape(4088, 1016, 32, 64, 2.0, "f32"), 14, {}),
+    ("small_t65_f32", LayerShape(136, 200, 16, 65, 2.0, "f32"), 15, {}),
 ]
 
 
