@@ -67,7 +67,7 @@ def _bits(t):
 
 
 CASES = [
-    ("crossover_bf16", synth.CONFIGS["crossover_bf16"], 1),      # 32.7 MiB of workspace
+    ("crossover_bf16", synth.CONFIGS["crossover_bf16"], 1),      # 7.0 MiB of workspace
     ("ragged_bf16", LayerShape(264, 520, 24, 37, 2.0, "bf16"), 2),
     ("tiny_f32", synth.CONFIGS["tiny_f32"], 3),
 ]
