@@ -246,7 +246,7 @@ def measure_peaks(torch, ops, dev):
 
 
 # Kernels of the factored norm (dora_norm's chain inside dora_forward).
-NORM_LABELS = ("gram_AAt", "gram_finalize", "cross_gram_proj", "norm_finalize", "row_norm")
+NORM_LABELS = ("gram_AAt", "gram_finalize", "cross_gram_proj", "row_norm")
 # Forward-only workloads reported beside the headline step (synth.CONFIGS names).
 FORWARD_CONFIGS = ("tiny_f32", "crossover_bf16", "highrank_bf16", "widemlp_bf16")
 

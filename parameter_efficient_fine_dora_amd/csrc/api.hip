@@ -106,6 +106,7 @@ int q_splits(const dora_shape& s) {
 struct Layout {
   size_t gpart = 0, ghi = 0, glo = 0, P = 0;     // norm
   size_t rowsq = 0, rowdot = 0;                  // norm: the projection's per-row partials
+  size_t done = 0;                               // norm: the projection's tile-row counters
   int64_t dot_parts = 0;
   size_t xs = 0, slora = 0;                      // forward
   size_t spart = 0;                              // forward of a small float32 layer: partials
@@ -158,6 +159,7 @@ Layout layout(const dora_shape& s, int op) {
       L.dot_parts = L.psplits * gemm_col_slots(p_cfg(s), s.r);
       L.rowsq = take((size_t)L.psplits * s.d_out * 4);
       L.rowdot = take((size_t)L.dot_parts * s.d_out * 4);
+      L.done = take((size_t)gemm_tile_rows(p_cfg(s), s.d_out) * 4);
     } else {
       L.P = take((size_t)L.psplits * s.d_out * r * 4);
     }
@@ -349,7 +351,8 @@ void give_scratch2(GemmProblem& g, void* ws, const Layout& L) {
 // Factored norm: G = A A^T (split-K), (s/2) G -> hi/lo, P = 2s W0 A^T + s^2 B G,
 // n_i = sqrt(||W0_i||^2 + B_i . P_i).  For bf16 the projection itself reduces
 // each row: it sums the squares of the W0 rows it streams and dots its
-// accumulators with B, so W0 crosses HBM once and P never reaches it.
+// accumulators with B, so W0 crosses HBM once and P never reaches it; the last
+// workgroup to finish each tile row then adds that row's partials into n.
 int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, float* norm,
              void* ws, const Layout& L, hipStream_t st) {
   const int dt = s.dtype;
@@ -363,7 +366,10 @@ int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, 
   if (fused_norm(s)) {
     const GramPlan gp = gram_bf16_plan(s.r, s.d_in);
     HIP_TRY(gram_bf16(A, s.r, s.d_in, gp, gpart, st));
-    HIP_TRY(gram_bf16_finish(gpart, gp, s.r, 0.5f * s.s, ghi, glo, nullptr, 0, st));
+    // the finisher also zeroes the projection's tile-row counters
+    HIP_TRY(gram_bf16_finish(gpart, gp, s.r, 0.5f * s.s, ghi, glo,
+                             reinterpret_cast<uint32_t*>(at(ws, L.done)),
+                             gemm_tile_rows(p_cfg(s), s.d_out), st));
   } else {
     GemmProblem g;
     g.M = g.N = s.r;
@@ -401,8 +407,10 @@ int run_norm(const dora_shape& s, const void* W0, const void* A, const void* B, 
     p.rowdot = rowdot;
     p.add = B;
     p.ld_add = s.r;
+    // the last workgroup of each tile row adds its rows' partials into n
+    p.norm_out = norm;
+    p.done = reinterpret_cast<uint32_t*>(at(ws, L.done));
     HIP_TRY(gemm(p, dt, st, "cross_gram_proj"));
-    HIP_TRY(norm_finalize(rowsq, L.psplits, rowdot, L.dot_parts, norm, s.d_out, st));
     return DORA_OK;
   }
   float* P = reinterpret_cast<float*>(at(ws, L.P));

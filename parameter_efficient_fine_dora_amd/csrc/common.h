@@ -30,4 +30,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Sum of n partials p[q * stride] in index order, loads issued eight at a time.
+__device__ __forceinline__ float sum_partials(const float* p, int64_t n, int64_t stride) {
+  float acc = 0.f;
+  int64_t q = 0;
+  for (; q + 8 <= n; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(q + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; q < n; ++q) acc += p[q * stride];
+  return acc;
+}
+
 }  // namespace dora

@@ -65,6 +65,8 @@ struct KArgs {
   int64_t ld_add;
   float* rowsq;          // kEpiNorm: [nsplit][M] sums of squares of opA over segment 0
   float* rowdot;         // kEpiNorm: [nsplit][tiles_n][M] row dots of alpha*C with `add`
+  float* norm_out;       // kEpiNorm: row norms written by the last workgroup of each tile row
+  uint32_t* done;        // kEpiNorm: [tiles_m] arrival counters, zero at launch
   int nsplit;            // K splits (the bf16 kernels' grid is tiles x nsplit, 1-D)
 };
 
@@ -562,6 +564,19 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[BM / WM / 32][BN / W
 // memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
+// Row-norm partials of the projection: atomic (write-through) stores when the
+// kernel finishes the norms itself and another workgroup reads them, plain
+// stores otherwise; and the matching agent-scope load.
+__device__ __forceinline__ void put_partial(float* dst, float v, const float* finishing) {
+  if (finishing)
+    __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *dst = v;
+}
+__device__ __forceinline__ float get_partial(const float* src) {
+  return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // NSEG: the most K segments the kernel walks (2, or 3 for the norm's projection
 // and the undetached-gradient products): every segment's pointers, strides
 // and bounds live in scalar registers, which the largest tiles have to spare.
@@ -847,7 +862,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
         float v = sq0[i];
         v += __shfl_xor(v, 32);
         const int m = m0 + wm * TM + i * 32 + lane;
-        if (lane < 32 && m < M) p.rowsq[(int64_t)split * M + m] = v;
+        if (lane < 32 && m < M) put_partial(p.rowsq + (int64_t)split * M + m, v, p.norm_out);
       }
     }
     const int64_t slot = (int64_t)split * p.tiles_n + tc.y;
@@ -895,7 +910,56 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
         float v = red[rr];
 #pragma unroll
         for (int w = 1; w < WN; ++w) v += red[w * BM + rr];
-        if (lane < 32 && m < M) p.rowdot[slot * M + m] = p.alpha * v;
+        if (lane < 32 && m < M) put_partial(p.rowdot + slot * M + m, p.alpha * v, p.norm_out);
+      }
+    }
+    if (p.norm_out) {
+      // The last workgroup of this tile row to finish (over K splits and
+      // column tiles) adds every partial of its rows in a fixed order:
+      // n_m = sqrt(max(0, sum_z rowsq[z][m] + sum_q rowdot[q][m])).  The
+      // partials travel as agent-scope atomic stores and loads, which write
+      // through and read past the per-XCD L2s; each workgroup waits for its
+      // stores to complete before it counts itself.  (Agent-scope fences would
+      // write back and invalidate the whole L2 instead, evicting the operand
+      // panels the other workgroups are still reading.)
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      int* last = reinterpret_cast<int*>(smem) + WN * BM;   // past `red`, which is done
+      if (tid == 0) {
+        const uint32_t before = __hip_atomic_fetch_add(p.done + tc.x, 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+        *last = before + 1 == (uint32_t)(p.nsplit * p.tiles_n);
+      }
+      __syncthreads();
+      if (*last) {
+        // Four lanes per row, each adding a contiguous quarter of the row's
+        // partials [rowsq z = 0..S-1, then rowdot q = 0..Q-1] with all of its
+        // loads in flight together; the quarters are then added in order.
+        const int nsq = p.nsplit, L = nsq + p.nsplit * p.tiles_n;
+        const int chunk = (L + 3) / 4, quarter = tid & 3;
+        const int j0 = quarter * chunk, j1 = min(L, j0 + chunk);
+        for (int rr = tid >> 2; rr < BM; rr += NT / 4) {   // whole 4-lane groups stay together
+          const int m = m0 + rr;
+          float part = 0.f;
+          if (m < M) {
+            for (int jb = j0; jb < j1; jb += 8) {
+              float v[8];
+#pragma unroll
+              for (int u = 0; u < 8; ++u) {
+                const int j = jb + u;
+                v[u] = j >= j1 ? 0.f
+                       : get_partial(j < nsq ? p.rowsq + (int64_t)j * M + m
+                                             : p.rowdot + (int64_t)(j - nsq) * M + m);
+              }
+#pragma unroll
+              for (int u = 0; u < 8; ++u) part += v[u];
+            }
+          }
+          const int base_lane = lane & ~3;
+          const float q0 = __shfl(part, base_lane), q1 = __shfl(part, base_lane + 1);
+          const float q2 = __shfl(part, base_lane + 2), q3 = __shfl(part, base_lane + 3);
+          if (quarter == 0 && m < M) p.norm_out[m] = sqrtf(fmaxf(((q0 + q1) + q2) + q3, 0.f));
+        }
       }
     }
     return;
@@ -1178,6 +1242,8 @@ int fill_args(const GemmProblem& p, KArgs& a) {
   a.ld_add = p.ld_add;
   a.rowsq = p.rowsq;
   a.rowdot = p.rowdot;
+  a.norm_out = p.norm_out;
+  a.done = p.done;
   return kt;
 }
 
@@ -1283,7 +1349,7 @@ hipError_t gemm(const GemmProblem& p, int dtype, hipStream_t st, const char* lab
 
   if (p.epi == kEpiNorm &&
       (dtype != kBF16 || !p.out_f32 || !p.a_kcontig || !p.b_kcontig || !p.rowsq || !p.rowdot ||
-       !p.add || p.N % 4 != 0 || p.nseg < 1 || p.seg[0].K <= 0))
+       !p.add || p.N % 4 != 0 || p.nseg < 1 || p.seg[0].K <= 0 || (p.norm_out && !p.done)))
     return hipErrorInvalidValue;
   if (dtype == kF32) {
     a.tiles_m = (int)cdiv64(p.M, 64);

@@ -47,6 +47,9 @@ struct GemmProblem {
   int64_t ld_add = 0;
   float* rowsq = nullptr;      // kEpiNorm: [split][M] float32 partial row sums of squares
   float* rowdot = nullptr;     // kEpiNorm: [gemm_col_slots * split][M] float32 partial row dots
+  float* norm_out = nullptr;   // kEpiNorm: if set, the row norms sqrt(max(0, sum rowsq + sum
+                               // rowdot)), formed by the last workgroup of each tile row
+  uint32_t* done = nullptr;    // kEpiNorm with norm_out: gemm_tile_rows counters, zero at launch
   // Library-chosen split-K (layer-dtype store epilogue only): float32 partial
   // sums go to `scratch`, then a fixed-order reduction writes C.
   void* scratch = nullptr;
@@ -125,11 +128,6 @@ hipError_t db_combine(const float* d1, int d1_splits, const float* q, int q_spli
 // [p_splits][d_out][r] (float32), ||W0_i||^2 streamed from W0.
 hipError_t row_norm(const void* W0, const void* B, const float* P, int p_splits, float* norm,
                     int64_t d_out, int64_t d_in, int64_t r, int dtype, hipStream_t st);
-
-// n_i = sqrt(max(0, sum_z rowsq[z][i] + sum_q rowdot[q][i])), both sums in
-// index order (the partials of the projection's kEpiNorm epilogue).
-hipError_t norm_finalize(const float* rowsq, int64_t n_sq, const float* rowdot, int64_t n_dot,
-                         float* norm, int64_t d_out, hipStream_t st);
 
 // y = base + ((g-1) base + g * slora) in place on y (base), slora = s * lora.
 hipError_t compose_fwd(void* y, const void* slora, const void* m, const float* norm, int64_t T,

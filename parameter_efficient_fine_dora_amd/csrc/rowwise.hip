@@ -53,21 +53,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Sum of n partials p[q * stride] in index order, loads issued eight at a time.
-__device__ __forceinline__ float sum_partials(const float* p, int64_t n, int64_t stride) {
-  float acc = 0.f;
-  int64_t q = 0;
-  for (; q + 8 <= n; q += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[(q + u) * stride];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u];
-  }
-  for (; q < n; ++q) acc += p[q * stride];
-  return acc;
-}
-
 // ---- Gram finisher ------------------------------------------------------------
 // part[z], z < splits: split-K partial sums of G = A A^T, added in a fixed
 // order.  Writes (s/2) G; bf16 layers get it as a hi + lo bf16 pair
@@ -147,18 +132,6 @@ __global__ __launch_bounds__(256) void dora_row_norm(const void* W0, const void*
   }
   const float tot = wave_sum((acc0 + acc1) + (acc2 + acc3));
   if (lane == 0) norm[row] = sqrtf(fmaxf(tot, 0.f));
-}
-
-// Row norms from the projection's per-row partials: thread = row, partial q of
-// every row contiguous, both sums in index order.
-__global__ __launch_bounds__(64) void dora_norm_finalize(const float* rowsq, int64_t n_sq,
-                                                         const float* rowdot, int64_t n_dot,
-                                                         float* norm, int64_t d_out) {
-  const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (row >= d_out) return;
-  const float base = sum_partials(rowsq + row, n_sq, d_out);
-  const float lora = sum_partials(rowdot + row, n_dot, d_out);
-  norm[row] = sqrtf(fmaxf(base + lora, 0.f));
 }
 
 // ---- compose forward ------------------------------------------------------------
@@ -593,14 +566,6 @@ hipError_t row_norm(const void* W0, const void* B, const float* P, int p_splits,
   else
     hipLaunchKernelGGL(dora_row_norm<false>, grid, dim3(256), 0, st, W0, B, P, p_splits, stride,
                        norm, d_out, d_in, r);
-  return hipGetLastError();
-}
-
-hipError_t norm_finalize(const float* rowsq, int64_t n_sq, const float* rowdot, int64_t n_dot,
-                         float* norm, int64_t d_out, hipStream_t st) {
-  LaunchTimer t("norm_finalize", st);
-  hipLaunchKernelGGL(dora_norm_finalize, dim3((unsigned)cdiv(d_out, 64)), dim3(64), 0, st, rowsq,
-                     n_sq, rowdot, n_dot, norm, d_out);
   return hipGetLastError();
 }
 

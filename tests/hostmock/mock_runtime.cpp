@@ -109,10 +109,6 @@ hipError_t row_norm(const void*, const void*, const float*, int, float*, int64_t
                     int, hipStream_t st) {
   return launch("row_norm", st);
 }
-hipError_t norm_finalize(const float*, int64_t, const float*, int64_t, float*, int64_t,
-                         hipStream_t st) {
-  return launch("norm_finalize", st);
-}
 hipError_t compose_fwd(void*, const void*, const void*, const float*, int64_t, int64_t, int,
                        hipStream_t st) {
   return launch("compose_fwd", st);

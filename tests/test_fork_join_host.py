@@ -16,7 +16,7 @@ MOCK = os.path.join(ROOT, "tests", "hostmock")
 CSRC = os.path.join(ROOT, "parameter_efficient_fine_dora_amd", "csrc")
 
 # every launch label of the forward and the detached backward
-LABELS = ["", "down_proj_xs", "gram_AAt", "gram_finalize", "cross_gram_proj", "norm_finalize",
+LABELS = ["", "down_proj_xs", "gram_AAt", "gram_finalize", "cross_gram_proj",
           "fused_fwd_gemm", "compose_bwd", "dm_finalize", "dB_gemm", "bg_scale", "t_proj",
           "dx_gemm", "dA_gemm"]
 
