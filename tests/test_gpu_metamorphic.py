@@ -7,6 +7,9 @@ output is exact in floating point, so the HIP path must reproduce it bit for bit
   not change (DoRA's magnitude/direction decoupling, DoRA reading notes Sec. 4.1).
 * Permuting the tokens permutes y, xs and dx (each token row is computed
   independently, with the K sum in a fixed order) and leaves the norm alone.
+* The same power-of-two scaling, repeated on one reused workspace, pins the
+  norm projection's cross-workgroup finish (the last workgroup of a tile row
+  reads the other workgroups' partial sums).
 """
 from __future__ import annotations
 
@@ -116,3 +119,38 @@ def test_near_cancelling_rows_recorded(ops):
     # the other rows are ordinary
     rest = slice(len(eps), None)
     assert np.max(np.abs(n[rest] - n_ref[rest]) / n_ref[rest]) <= 1e-3
+
+
+REUSE = [
+    # r in 257..384: one 128 x 384 tile per row block, K split nine ways
+    ("rank320_bf16", LayerShape(2048, 4096, 320, 1, 2.0, "bf16")),
+    # two column tiles of the generic 128 x 128 plan
+    ("rank200_bf16", LayerShape(1032, 2056, 200, 1, 2.0, "bf16")),
+    # 64 tile rows
+    ("rank64_bf16", LayerShape(8192, 1024, 64, 1, 2.0, "bf16")),
+]
+
+
+@pytest.mark.parametrize("name,shape", REUSE, ids=[c[0] for c in REUSE])
+def test_norm_calls_on_one_workspace(ops, name, shape):
+    """dora_norm called over and over on ONE workspace, W0 and B scaled by a
+    different power of two each time: the norms scale by exactly that factor
+    (every term of n^2 scales by its square), so a row norm formed from any
+    partial sum left in the workspace by the previous call, or read before
+    another workgroup's partial landed, shows up as a bit difference.  The
+    first call is checked against the oracle."""
+    from parameter_efficient_fine_dora_amd import _lib
+    say(f"repeated dora_norm on one workspace: {name} {shape}")
+    layer = synth.make_layer(shape, 71)
+    dev = layer_to_device(layer, "bf16")
+    sh = _lib.shape(shape.d_out, shape.d_in, shape.r, 0, _lib.BF16, shape.s)
+    ws = torch.empty(_lib.workspace_bytes(sh, _lib.OP_NORM), dtype=torch.uint8, device="cuda")
+    base = ops.dora_norm(dev["W0"], dev["A"], dev["B"], shape.s, workspace=ws).clone()
+    torch.cuda.synchronize()
+    L = synth.layer_f64(layer, "bf16")
+    n_ref = oracle.dora_norm(L["W0"], L["A"], L["B"], shape.s)
+    assert np.max(np.abs(download(base) - n_ref) / n_ref) <= 1e-3
+    for c in (2.0, 0.5, 4.0, 1.0, 0.25, 8.0, 1.0, 2.0):
+        n = ops.dora_norm(dev["W0"] * c, dev["A"], dev["B"] * c, shape.s, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(n, base * c), f"scale {c}"
