@@ -684,9 +684,10 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
   const DmRecompute zr{norm, grad_y, x, W0, A, B, s.s, s.tokens, s.d_in, s.r};
 
   // With the norm detached, ts runs on the side stream beside the compose
-  // backward (one HBM-bound, the other latency-bound); dx waits for both.  The
-  // rest follows dx on the caller's stream: dx fills the chip in whole rounds
-  // of workgroups, and anything beside it only delays its second round.
+  // backward, dm's finisher and dB (which need only gz and xs); dx waits for
+  // all of them.  dA follows dx on the caller's stream: dx fills the chip in
+  // whole rounds of workgroups, and anything beside it only delays its second
+  // round.
   SideStream* side = (!exact && need_ts) ? side_stream() : nullptr;
   SideFork fk(side, st);
   if (side) {
@@ -695,8 +696,15 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
   }
   if (need_gz || dm)
     HIP_TRY(compose_bwd(grad_y, y, m, norm, gz, dmpart, s.tokens, s.d_out, kTokPerDmBlock, dt, st));
-  HIP_TRY(fk.join());   // dx below needs ts
+  // dm and dB need only the compose backward's outputs (and the caller's xs),
+  // so they run before the join, beside the side stream's chain.
   if (dm) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, zr, dt, st));
+  bool db_done = false;
+  if (side && grad_B && has_r && xs && !noT) {
+    DORA_CHECK(grad_b(xs));
+    db_done = true;
+  }
+  HIP_TRY(fk.join());   // dx below needs ts
 
   // A.1 terms: k' = -s m dm / n^2, Bk' = diag(k') B, Q = W0 A^T + s B G,
   // H' = s Bk'^T B.  Then dB += diag(k') Q and dA += Bk'^T W0 + H' A.
@@ -772,7 +780,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
     HIP_TRY(gemm(d, dt, st, "dx_gemm"));
   }
 
-  if (grad_B && has_r) {
+  if (grad_B && has_r && !db_done) {
     const void* xsu = xs;
     if (!xsu && !noT) {
       void* xw = at(ws, L.xs);
