@@ -1109,7 +1109,7 @@ constexpr Cfg kCfgs[] = {
     {128, 384, 2, 4, 2},   // 6: 8 waves, 64x96 per wave (N = rank 384 in one tile)
     {384, 128, 4, 2, 2},   // 7: 8 waves, 96x64 per wave (M = rank 384 in one tile)
     {128, 192, 2, 2, 2},   // 8: 4 waves, 64x96 per wave (two workgroups per CU; K-contiguous only)
-    {128, 128, 2, 2, 3},   // 9: as 2 with three stages (one workgroup per CU)
+    {128, 128, 4, 2, 3},   // 9: 8 waves, 32x64 per wave, three stages (one workgroup per CU)
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -1187,7 +1187,7 @@ hipError_t launch_cfg(int cfg, bool akc, bool bkc, const KArgs& a, int epi, bool
     case 6: return launch_layout<128, 384, 2, 4, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 7: return launch_layout<384, 128, 4, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
     case 8: return launch_layout<128, 192, 2, 2, 2>(akc, bkc, a, epi, out_f32, grid, st);
-    case 9: return launch_layout<128, 128, 2, 2, 3>(akc, bkc, a, epi, out_f32, grid, st);
+    case 9: return launch_layout<128, 128, 4, 2, 3>(akc, bkc, a, epi, out_f32, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
