@@ -58,12 +58,39 @@ KERNEL_SOURCES = ["include/dora.h"] + [
 WORKLOAD_TAG = "highrank_d8192_r384_t4096"
 
 
+def code_tokens(text: str) -> str:
+    """C/C++/HIP source with its comments removed and whitespace runs collapsed
+    (string and character literals kept as written), so that an edit to the
+    comments alone leaves it unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                           # literal: copy through its closing quote
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the library sources: recorded counter data applies only to the sources it was taken from."""
+    """sha256 over the library sources' code (comments and whitespace aside):
+    recorded counter data applies only to the code it was taken from."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(rel.encode() + b"\0" + code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,7 +8,7 @@
  *     y   = x (diag(m / n) V')^T   (layer output)
  *
  * (DoRA reading notes, zhongzhuzhou.org: Sec. 3.1 eq. (6) and Sec. 3.2
- * Algorithm 1 steps 7-11; Scaling DoRA summary page, gptget.net, arXiv
+ * Algorithm 1; Scaling DoRA summary page, gptget.net, arXiv
  * 2603.22276, abstract, for the row-wise norm of W + sBA and the scale s.)
  *
  * The library never forms the d_out x d_in product B A.  The norm is
@@ -107,7 +107,7 @@ DORA_API size_t dora_workspace_bytes(const dora_shape* shape, int op);
 /*
  * Row norms n_i = || W0_i + s (B A)_i ||, in factored form (Scaling DoRA
  * abstract: base, cross and Gram terms through O(d_out r + r^2)
- * intermediates; DoRA reading notes Algorithm 1 step 9, per output row).
+ * intermediates; DoRA reading notes Algorithm 1, per output row).
  *   W0, A, B   inputs (layer dtype); A and B may be NULL when r == 0
  *   norm_out   output, float32 [d_out]
  *   ws         workspace of at least dora_workspace_bytes(shape, DORA_OP_NORM)
@@ -116,7 +116,7 @@ DORA_API int dora_norm(const dora_shape* shape, const void* W0, const void* A, c
                        float* norm_out, void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
- * Forward of a DoRA linear layer (DoRA reading notes Algorithm 1 steps 7-11):
+ * Forward of a DoRA linear layer (DoRA reading notes Algorithm 1):
  *   norm_out = n (float32 [d_out], as dora_norm),
  *   xs_out   = s * (x A^T)                  [T, r], layer dtype; NULL = not kept,
  *   y        = g * (x W0^T + xs B^T) with g = m / max(n, 1e-8),
@@ -182,7 +182,7 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
                            void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
- * Merged weight for deployment (DoRA reading notes, Algorithm 1 steps 16-17;
+ * Merged weight for deployment (DoRA reading notes, Algorithm 1;
  * Sec. 3.1 eq. (6)): the dense layer that replaces the adapted one,
  *   W_out_i = g_i * (W0_i + s (B A)_i),  g_i = m_i / max(n_i, 1e-8),
  * so that x W_out^T equals dora_forward's y.  One GEMM, B . A over K = r, whose

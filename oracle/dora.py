@@ -12,7 +12,7 @@ Sources (cited by page title and section):
         abstract: row-wise norm of W + sBA over a dense [d_out, d_in] product;
         the factored base / cross / Gram terms.
   [DN]  DoRA reading notes (zhongzhuzhou.org): Sec. 3.1 eq. (6); Sec. 3.2
-        Algorithm 1 (steps 7-18); Sec. 3.3 eq. (7), (8); Sec. 3.4 (detach);
+        Algorithm 1; Sec. 3.3 eq. (7), (8); Sec. 3.4 (detach);
         Sec. 3.5 (DVoRA: the direction update of VeRA); Appendix A.1 eq. (A.1).
 
 Conventions (readings where the pages disagree or are silent):
@@ -50,23 +50,23 @@ def _f64(a):
 
 
 def lora_update(A, B):
-    """Delta V = B @ A, the low-rank direction update ([DN] Alg. 1 step 7)."""
+    """Delta V = B @ A, the low-rank direction update ([DN] Alg. 1)."""
     return _f64(B) @ _f64(A)
 
 
 def adapted_direction(W0, A, B, s):
-    """V' = W0 + s * B @ A ([DN] Alg. 1 step 8 with [SD]'s scale s)."""
+    """V' = W0 + s * B @ A ([DN] Alg. 1 with [SD]'s scale s)."""
     return _f64(W0) + float(s) * lora_update(A, B)
 
 
 def row_norms(V):
-    """n_i = sqrt(sum_k V_ik^2), one per output row ([DN] Alg. 1 step 9; [SD])."""
+    """n_i = sqrt(sum_k V_ik^2), one per output row ([DN] Alg. 1; [SD])."""
     V = _f64(V)
     return np.sqrt(np.sum(V * V, axis=1))
 
 
 def magnitude_scale(m, n):
-    """g_i = m_i / n_i, with n clamped at NORM_EPS ([DN] Alg. 1 step 10)."""
+    """g_i = m_i / n_i, with n clamped at NORM_EPS ([DN] Alg. 1)."""
     return _f64(m) / np.maximum(_f64(n), NORM_EPS)
 
 
@@ -76,14 +76,14 @@ def dora_norm(W0, A, B, s):
 
 
 def merged_weight(W0, A, B, m, s):
-    """W' = m * V' / ||V'||_row ([DN] eq. 6; Alg. 1 steps 10 and 16)."""
+    """W' = m * V' / ||V'||_row ([DN] eq. 6; Alg. 1)."""
     V = adapted_direction(W0, A, B, s)
     g = magnitude_scale(m, row_norms(V))
     return g[:, None] * V
 
 
 def dora_forward(x, W0, A, B, m, s, norm=None):
-    """y = x @ W'^T with W' the merged DoRA weight ([DN] Alg. 1 step 11).
+    """y = x @ W'^T with W' the merged DoRA weight ([DN] Alg. 1).
 
     ``norm`` substitutes fixed row norms for the computed ones: the value a
     detached norm contributes while it is held constant ([DN] Sec. 3.4).
@@ -128,7 +128,7 @@ def scaled_down_projection(x, A, s):
     """s * (x @ A^T): the rank-r activations of the low-rank branch, scaled.
 
     The forward's output splits as y = g * (x W0^T + s (x A^T) B^T) because
-    V' = W0 + s B A ([DN] Alg. 1 steps 8 and 11); this is the factor
+    V' = W0 + s B A ([DN] Alg. 1); this is the factor
     s (x A^T) that a fast implementation keeps for the backward.
     """
     return float(s) * (_f64(x) @ _f64(A).T)

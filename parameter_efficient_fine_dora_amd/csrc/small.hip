@@ -1,6 +1,6 @@
 // The whole forward of a small float32 DoRA layer in two kernels (Scaling DoRA
 // summary page, English abstract: the factored norm and the single-pass
-// compose; DoRA reading notes, Alg. 1 steps 7-11).  Layers this small are all
+// compose; DoRA reading notes, Alg. 1).  Layers this small are all
 // launch latency on the multi-kernel path.  Here one pass over K = d_in
 // accumulates, for each block of 16 output rows,
 //   xs = x A^T (before the scale by s), z_t,i = x_t . W0_i,

@@ -38,8 +38,8 @@ class DoRAFunction(torch.autograd.Function):
 class DoRALinear(torch.nn.Module):
     """y = (m / ||W0 + s B A||_row) * (x W0^T + s (x A^T) B^T), W0 frozen.
 
-    Initialised as DoRA starts training (DoRA reading notes, Algorithm 1
-    steps 1-4): m = row norms of W0, A Kaiming-uniform, B = 0.
+    Initialised as DoRA starts training (DoRA reading notes, Algorithm 1):
+    m = row norms of W0, A Kaiming-uniform, B = 0.
     """
 
     def __init__(self, weight: torch.Tensor, r: int, s: float = 2.0, flags: int = 0):

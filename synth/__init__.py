@@ -13,7 +13,7 @@ Distributions (all dense, iid, per layer):
   W0 ~ N(0, 0.02^2)            frozen base weight      [d_out, d_in]
   A  ~ U(-1/sqrt(d_in), +1/sqrt(d_in))   LoRA down     [r, d_in]
        (fan-in scaled Kaiming-uniform; DoRA reading notes, Sec. 1.3 and
-        Algorithm 1 step 3 name Kaiming-uniform without a bound)
+        Algorithm 1 name Kaiming-uniform without a bound)
   B  ~ N(0, 0.01^2)            LoRA up                 [d_out, r]
   m_i = ||W0_i|| * (1 + U(-0.05, 0.05))   magnitude    [d_out]
        (||W0_i|| from the already-rounded W0; m then rounded itself)
@@ -109,7 +109,7 @@ def make_layer(shape: LayerShape, seed: int | None = None, *, grad: bool = False
     Returns a dict of contiguous numpy arrays: W0, A, B, m, x and (grad=True) gy,
     each uint16 bf16 bits or float32 per ``shape.dtype``.  ``b_std`` selects the
     "large-B" stress distribution (e.g. 0.1) and ``zero_b`` the B = 0 start of
-    training (DoRA reading notes, Algorithm 1 step 4).
+    training (DoRA reading notes, Algorithm 1).
     """
     if seed is None:
         seed = CONFIG_SEED.get(shape.name, 0)

@@ -267,7 +267,7 @@ def pin_sampled_forms(orc):
 
 
 def pin_merged_weight(orc):
-    """The deploy-time merge (Alg. 1 step 16): every row of W'_merged has norm m_i and
+    """The deploy-time merge (Alg. 1): every row of W'_merged has norm m_i and
     direction V'_i; with B = 0 and m = ||W0_i|| it is W0 itself; x W'_merged^T is the
     layer output."""
     W0, A, B, m, x, _ = _layer(11)

@@ -62,6 +62,15 @@ def test_kernel_source_hash_is_stable():
     assert bench.kernel_source_hash() == h
 
 
+def test_code_tokens_drop_comments_only():
+    """The source hash sees code, not comments: comments and whitespace runs go,
+    string and character literals (even ones holding comment markers) stay."""
+    src = "int a = 1; // note\n/* block\n comment */ const char* s = \"x // y /* z */\";\nchar c = '/';"
+    assert bench.code_tokens(src) == "int a = 1; const char* s = \"x // y /* z */\"; char c = '/';"
+    assert bench.code_tokens("a  +\n\tb") == bench.code_tokens("a + b")
+    assert bench.code_tokens("a + b") != bench.code_tokens("a - b")
+
+
 def test_recorded_traffic_belongs_to_these_sources():
     """Counter data recorded for other sources is never reported: the traffic
     table is either empty or carries bytes for the step's kernels."""
