@@ -683,9 +683,9 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
   // columns with m_i == 0 take dm from its definition (y / m = z / n fails there)
   const DmRecompute zr{norm, grad_y, x, W0, A, B, s.s, s.tokens, s.d_in, s.r};
 
-  // With the norm detached, ts runs on the side stream beside the compose
-  // backward, dm's finisher and dB (which need only gz and xs); dx waits for
-  // all of them.  dA follows dx on the caller's stream: dx fills the chip in
+  // With the norm detached, ts and then dm's finisher run on the side stream
+  // beside the compose backward and dB (which need only gz and xs); dx waits
+  // for all of them.  dA follows dx on the caller's stream: dx fills the chip in
   // whole rounds of workgroups, and anything beside it only delays its second
   // round.
   SideStream* side = (!exact && need_ts) ? side_stream() : nullptr;
@@ -697,8 +697,14 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
   if (need_gz || dm)
     HIP_TRY(compose_bwd(grad_y, y, m, norm, gz, dmpart, s.tokens, s.d_out, kTokPerDmBlock, dt, st));
   // dm and dB need only the compose backward's outputs (and the caller's xs),
-  // so they run before the join, beside the side stream's chain.
-  if (dm) HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, zr, dt, st));
+  // so they run before the join: dm's finisher on the side stream after ts
+  // (a second fork makes it wait for the compose backward), dB on the caller's.
+  if (dm && side) {
+    HIP_TRY(fk.fork());
+    HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, zr, dt, fk.side()));
+  } else if (dm) {
+    HIP_TRY(dm_finalize(dmpart, L.dm_blocks, m, dm, s.d_out, zr, dt, st));
+  }
   bool db_done = false;
   if (side && grad_B && has_r && xs && !noT) {
     DORA_CHECK(grad_b(xs));
