@@ -151,8 +151,8 @@ SMALL = [
     # rank 32, d_out and d_in just under their limits), and one token past it
     ("smallmax_f32", LayerShape(4088, 1016, 32, 64, 2.0, "f32"), 14, {}),
     ("small_t65_f32", LayerShape(136, 200, 16, 65, 2.0, "f32"), 15, {}),
-    # one token, rank one, a single K chunk and a single row block
-    ("small_t1_r1_f32", LayerShape(16, 64, 1, 1, 2.0, "f32"), 16, {}),
+    # one token, the smallest nonzero rank, one K chunk and one row block
+    ("small_t1_r8_f32", LayerShape(16, 64, 8, 1, 2.0, "f32"), 16, {}),
     # rank 32 with B = 0 (the start of training): the norm is ||W0_i|| and y = m-scaled base
     ("small_zeroB_f32", LayerShape(72, 136, 32, 5, 2.0, "f32"), 17, dict(zero_b=True)),
 ]
