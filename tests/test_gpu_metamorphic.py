@@ -9,7 +9,9 @@ output is exact in floating point, so the HIP path must reproduce it bit for bit
   independently, with the K sum in a fixed order) and leaves the norm alone.
 * The same power-of-two scaling, repeated on one reused workspace, pins the
   norm projection's cross-workgroup finish (the last workgroup of a tile row
-  reads the other workgroups' partial sums).
+  reads the other workgroups' partial sums); A scaled by c with B by 1/c leaves
+  every norm unchanged while G scales, which pins the Gram matrix each call
+  forms afresh in the same workspace.
 """
 from __future__ import annotations
 
@@ -154,3 +156,10 @@ def test_norm_calls_on_one_workspace(ops, name, shape):
         n = ops.dora_norm(dev["W0"] * c, dev["A"], dev["B"] * c, shape.s, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(n, base * c), f"scale {c}"
+    # A scaled by c and B by 1/c: BA, and so every norm, is bitwise unchanged, while
+    # G = A A^T (formed again by each call) scales by c^2, so a Gram term built
+    # from the previous call's G or its partial sums shows up as a bit difference.
+    for c in (2.0, 0.5, 4.0, 0.25, 1.0, 8.0):
+        n = ops.dora_norm(dev["W0"], dev["A"] * c, dev["B"] / c, shape.s, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(n, base), f"A scaled by {c}"
