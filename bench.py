@@ -47,7 +47,7 @@ if ROOT not in sys.path:
 METRIC = "DoRA layer fwd+bwd µs & norm/compose GB/s (% HBM peak), d=8192 r=384 bf16"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFS = 2500.0         # MI355X dense bf16 MFMA, TFLOP/s
-FP32_PEAK_TFS = 157.3          # MI355X fp32 vector, TFLOP/s (the fp32 layers' GEMMs run on the VALU)
+FP32_PEAK_TFS = 157.3          # MI355X fp32 vector / matrix, TFLOP/s (the fp32 layers' GEMMs run on fp32 MFMA)
 DEFAULT_CONFIG = "highrank_bwd_bf16"
 
 
@@ -598,7 +598,10 @@ def main():
         roof = None
     elif kind == "flop":
         achieved = amount / avg_s / 1e12
-        roof = {"bound": "mfma" if is_bf else "alu", "achieved": round(achieved, 2),
+        # every GEMM runs on the matrix cores (bf16, or fp32 MFMA for float32 layers);
+        # the two-kernel small float32 forward runs on the vector ALUs
+        on_alu = dominant.startswith("small_")
+        roof = {"bound": "alu" if on_alu else "mfma", "achieved": round(achieved, 2),
                 "peak": flop_peak,
                 "unit": "TFLOP/s", "frac": round(achieved / flop_peak, 4),
                 "traffic": traffic.get(dominant, {}).get("total_bytes"),

@@ -1,7 +1,7 @@
 // Dense contractions of the DoRA hot path on gfx950.
 //
 // bf16 operands run on the CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16,
-// float32 accumulation); float32 layers use a VALU tile kernel.  One kernel
+// float32 accumulation); float32 layers use v_mfma_f32_32x32x2_f32 tiles.  One kernel
 // template covers every contraction of the path:
 //   C[m, n] = alpha * sum over segments s, k < K_s of opA_s(m, k) * opB_s(n, k)
 // where each operand is either K-contiguous or M/N-contiguous in memory, and
@@ -975,20 +975,31 @@ __global__ __launch_bounds__(WM * WN * 64) void dora_gemm_bf16(const KArgs p) {
                                                 wn, lane);
 }
 
-// float32 layers: 64x64 tiles, 16-deep K steps, 4x4 outputs per thread.
+// float32 layers: 64x64 tiles on the fp32 matrix cores (v_mfma_f32_32x32x2_f32),
+// one 32x32 block per wave.  A 64-deep K step is staged through registers into
+// k-major LDS tiles (every load of the step in flight before the first LDS
+// store, so a step costs one memory latency); step pair (2j, 2j+1) is one
+// MFMA whose lanes 0-31 take k = 2j and lanes 32-63 k = 2j + 1 of their row.
+// As in the bf16 kernels the MFMA is issued as opB-block x opA-block^T, so each
+// lane ends up holding four consecutive output columns of one output row.
 template <bool AKC, bool BKC, int EPI>
 __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
   constexpr int BM = 64, BN = 64, BKF = kBK;   // one 64-deep step per pass through LDS
   constexpr int kPer = BM * BKF / 256;          // elements of each operand per thread and pass
   __shared__ float As[BKF][BM + 4];
   __shared__ float Bs[BKF][BN + 4];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;      // the wave's 32x32 block of the tile
   const int2 tc = tile_coords(p.tiles_m, p.tiles_n);
   const int m0 = tc.x * BM, n0 = tc.y * BN;
-  float acc[4][4] = {};
+  f32x16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   const int kt_total = p.kt_total;   // in 64-deep units, shared with the bf16 path
   const int kt_lo = blockIdx.y * p.kt_per_split;
   const int kt_hi = min(kt_lo + p.kt_per_split, kt_total);
+  const int ra = wm * 32 + (lane & 31), rb = wn * 32 + (lane & 31), kh = lane >> 5;
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
     const int s = kt < p.kt_end[0] ? 0 : (kt < p.kt_end[1] ? 1 : 2);
     const int k0 = (kt - (s == 0 ? 0 : (s == 1 ? p.kt_end[0] : p.kt_end[1]))) * kBK;
@@ -997,9 +1008,8 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
     const int64_t lda = s == 0 ? p.lda[0] : (s == 1 ? p.lda[1] : p.lda[2]);
     const int64_t ldb = s == 0 ? p.ldb[0] : (s == 1 ? p.ldb[1] : p.ldb[2]);
     const int Ks = s == 0 ? p.K[0] : (s == 1 ? p.K[1] : p.K[2]);
-    // Every load of the pass is issued before the first LDS store, so a
-    // pass costs one memory latency.  Element e of a K-contiguous operand is
-    // (row e / 64, k e % 64): 64 lanes read one row's 256 contiguous bytes.
+    // Element e of a K-contiguous operand is (row e / 64, k e % 64): 64 lanes
+    // read one row's 256 contiguous bytes.
     float va[kPer], vb[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -1023,38 +1033,29 @@ __global__ __launch_bounds__(256) void dora_gemm_f32(const KArgs p) {
     }
     __syncthreads();
 #pragma unroll 8
-    for (int kk = 0; kk < BKF; ++kk) {
-      float ra[4], rb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ra[i] = As[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rb[j] = Bs[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ra[i], rb[j], acc[i][j]);
-    }
+    for (int j = 0; j < BKF / 2; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Bs[2 * j + kh][rb], As[2 * j + kh][ra], acc, 0, 0, 0);
     __syncthreads();
   }
+  // acc[v]: row m = m0 + wm*32 + lane%32, column n = n0 + wn*32 + (v/4)*8 + (lane/32)*4 + v%4
   float* c = reinterpret_cast<float*>(p.c) + blockIdx.y * p.split_stride;
-  const int n = n0 + tx * 4;
-  if (n >= p.N) return;
-  f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
-  if (EPI == kEpiCompose) gm1 = gm1_4<false>(p.mag, p.norm, n);
+  const int m = m0 + ra;
+  if (m >= p.M) return;
+  float gr = 0.f;
+  if (EPI == kEpiMerge) gr = g_row<false>(p.mag, p.norm, m);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty * 4 + i;
-    if (m >= p.M) continue;
+  for (int g = 0; g < 4; ++g) {
+    const int n = n0 + wn * 32 + g * 8 + kh * 4;
+    if (n >= p.N) continue;   // N % 4 == 0: n < N covers n..n+3
+    f32x4 gm1 = {0.f, 0.f, 0.f, 0.f};
+    if (EPI == kEpiCompose) gm1 = gm1_4<false>(p.mag, p.norm, n);
     f32x4 w = {0.f, 0.f, 0.f, 0.f};
-    float gr = 0.f;
-    if (EPI == kEpiMerge) {
+    if (EPI == kEpiMerge)
       w = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.add) + (int64_t)m * p.ld_add + n);
-      gr = g_row<false>(p.mag, p.norm, m);
-    }
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float z = p.alpha * acc[i][e];
+      const float z = p.alpha * acc[g * 4 + e];
       v[e] = (EPI == kEpiMerge) ? gr * (w[e] + z) : ((EPI == kEpiCompose) ? z + gm1[e] * z : z);
     }
     store4<true>(c, p.ldc, m, n, v[0], v[1], v[2], v[3]);
@@ -1265,7 +1266,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bk
   if (M <= 0 || N <= 0) return {-1, 1};
   const int64_t ktiles = cdiv64(K, kBK);
   if (dtype == kF32) {
-    // 64 x 64 VALU tiles (one wave per SIMD, latency-bound per workgroup): split K,
+    // 64 x 64 fp32-MFMA tiles (one wave per SIMD, latency-bound per workgroup): split K,
     // down to one 64-deep step per split, up to ~256 workgroups
     const int64_t t = cdiv64(M, 64) * cdiv64(N, 64);
     int64_t split = std::min<int64_t>((256 + t - 1) / t, std::max<int64_t>(1, ktiles));

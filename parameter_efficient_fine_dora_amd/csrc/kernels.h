@@ -59,7 +59,7 @@ struct GemmProblem {
 };
 
 struct GemmPlan {
-  int cfg;     // tile configuration index (-1: float32 VALU kernel)
+  int cfg;     // tile configuration index (-1: the float32 kernel)
   int split;   // split-K factor
 };
 
