@@ -1266,10 +1266,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool akc, bool bk
   if (M <= 0 || N <= 0) return {-1, 1};
   const int64_t ktiles = cdiv64(K, kBK);
   if (dtype == kF32) {
-    // 64 x 64 fp32-MFMA tiles (one wave per SIMD, latency-bound per workgroup): split K,
-    // down to one 64-deep step per split, up to ~256 workgroups
+    // 64 x 64 fp32-MFMA tiles (one wave per SIMD, latency-bound per workgroup; three
+    // fit a CU): split K, down to one 64-deep step per split, up to ~768 workgroups
     const int64_t t = cdiv64(M, 64) * cdiv64(N, 64);
-    int64_t split = std::min<int64_t>((256 + t - 1) / t, std::max<int64_t>(1, ktiles));
+    int64_t split = std::min<int64_t>((768 + t - 1) / t, std::max<int64_t>(1, ktiles));
     return {-1, (int)std::max<int64_t>(1, std::min<int64_t>(split, 16))};
   }
   auto tiles = [&](int cfg) { return cdiv64(M, kCfgs[cfg].bm) * cdiv64(N, kCfgs[cfg].bn); };
