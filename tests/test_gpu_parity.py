@@ -180,6 +180,39 @@ def test_fullrank_large_tile_transposed_products(ops):
     compare_full(shape, layer, got)
 
 
+TAIL = [
+    # fused forward on 4 x 65 tiles of 256 x 256 over K = 2080: the last round (4 tiles) is
+    # the last tile column, which runs as a second launch on 256 x 128 tiles
+    ("fwd_tail", LayerShape(16640, 2056, 24, 1024, 2.0, "bf16"), 41),
+    # dx (W0 read transposed) on 4 x 65 tiles over K = 2080, ragged d_out
+    ("dx_tail", LayerShape(2040, 16640, 40, 1024, 2.0, "bf16"), 42),
+]
+
+
+@pytest.mark.parametrize("name,shape,seed", TAIL, ids=[c[0] for c in TAIL])
+def test_tail_columns_on_narrower_tiles(ops, name, shape, seed):
+    """A large-tile GEMM whose last round of workgroups is at most half full runs
+    that round's tile columns on 256 x 128 tiles; every output matches the oracle
+    in full (and the merged weight of the same layer does too)."""
+    say(f"tail columns {name} shape={shape}")
+    layer = synth.make_layer(shape, seed, grad=True)
+    got = run_layer(ops, shape, layer)
+    compare_full(shape, layer, got)
+    # the split is taken: the GEMM runs as two launches (timing hook, serial order)
+    ops.timing_enable(True)
+    try:
+        run_layer(ops, shape, layer)
+        rec = ops.timing_collect()
+    finally:
+        ops.timing_enable(False)
+    label = "fused_fwd_gemm" if name == "fwd_tail" else "dx_gemm"
+    assert rec[label][0] == 2, rec
+    dev = layer_to_device(layer, "bf16")
+    W = download(ops.dora_merge(dev["W0"], dev["A"], dev["B"], dev["m"], shape.s))
+    L = synth.layer_f64(layer, "bf16")
+    check_out(W, oracle.merged_weight(L["W0"], L["A"], L["B"], L["m"], shape.s), "merged weight")
+
+
 def test_skip_outputs_and_recompute_xs(ops):
     shape = LayerShape(264, 520, 24, 37, 2.0, "bf16")
     layer = synth.make_layer(shape, 11, grad=True)
