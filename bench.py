@@ -327,13 +327,17 @@ def timed_series(torch, run, steps):
     """K back-to-back steps with an event between consecutive steps: the total
     (first to last event) and every step's own duration come from one series."""
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    host = [0.0] * (steps + 1)
     torch.cuda.synchronize()
+    host[0] = time.perf_counter()
     evs[0].record()
     for k in range(steps):
         run()
         evs[k + 1].record()
+        host[k + 1] = time.perf_counter()
     torch.cuda.synchronize()
     per = [evs[k].elapsed_time(evs[k + 1]) for k in range(steps)]
+    timed_series.host_ms = [(host[k + 1] - host[k]) * 1e3 for k in range(steps)]
     return evs[0].elapsed_time(evs[-1]) / steps, per
 
 
@@ -530,6 +534,12 @@ def main():
     wall = time.perf_counter() - t0
     spread = step_stats(per)
     spread["first_steps_us"] = [round(v * 1e3, 1) for v in per[:5]]
+    if not args.cold:
+        # host time to enqueue each step (the library's launches and events); a
+        # step whose enqueue takes longer than the GPU's work leaves the GPU waiting
+        hms = timed_series.host_ms
+        spread["host_enqueue_us"] = {"median": round(float(np.median(hms)) * 1e3, 1),
+                                     "first_steps": [round(v * 1e3, 1) for v in hms[:5]]}
 
     # per-kernel times: the same steps again, each launch bracketed by HIP events
     print("# per-kernel timing", file=sys.stderr, flush=True)
