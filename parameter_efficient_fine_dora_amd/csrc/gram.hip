@@ -151,11 +151,12 @@ __global__ __launch_bounds__(256) void dora_gram_partial(const uint16_t* A, int 
 }
 
 // Workgroup (tile, g) finishes rows 4g .. 4g + 3 of an upper-triangle tile: each
-// thread adds one element's split sums in split order (coalesced, eight loads
-// in flight) and writes the scaled hi + lo pair at (i, j) and at the mirror
+// thread adds one element's split sums in split order (coalesced, every load
+// in flight before the first add; at most kGMaxSplits) and writes the scaled hi + lo pair at (i, j) and at the mirror
 // (j, i).  On a diagonal tile only the elements on or above the diagonal are
 // taken, each written to both places, so G comes out exactly symmetric.
 constexpr int kGFinRows = 4;
+constexpr int kGMaxSplits = 32;
 __global__ __launch_bounds__(256) void dora_gram_finish(const float* part, int splits, int r,
                                                         float scale, uint16_t* g_hi,
                                                         uint16_t* g_lo, uint32_t* zero,
@@ -173,16 +174,13 @@ __global__ __launch_bounds__(256) void dora_gram_finish(const float* part, int s
   if (i >= r || j >= r) return;
   const float* p = part + (int64_t)blockIdx.x * splits * kGT * kGT + a * kGT + b;
   constexpr int64_t kS = kGT * kGT;
-  float s = 0.f;
-  int z = 0;
-  for (; z + 8 <= splits; z += 8) {
-    float v[8];
+  float part_v[kGMaxSplits];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[(z + u) * kS];
+  for (int u = 0; u < kGMaxSplits; ++u) part_v[u] = u < splits ? p[u * kS] : 0.f;
+  float s = part_v[0];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s = (z + u == 0) ? v[u] : s + v[u];
-  }
-  for (; z < splits; ++z) s = z == 0 ? p[0] : s + p[z * kS];
+  for (int u = 1; u < kGMaxSplits; ++u)
+    if (u < splits) s += part_v[u];
   const float v = scale * s;
   const uint16_t hi = f32_to_bf16(v);
   const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
@@ -202,10 +200,12 @@ GramPlan gram_bf16_plan(int64_t r, int64_t d_in) {
   GramPlan g{};
   const int64_t nt = cdiv(r, kGT);
   g.tiles = nt * (nt + 1) / 2;
-  // about 320 workgroups (two fit a CU), K chunks a whole number of stages
+  // At most about 256 workgroups, so that no CU takes two; K chunks a whole
+  // number of stages.  Measured at r = 384, d_in = 8192 (21 tiles): 12 chunks
+  // (252 workgroups) 10.5 us, 16 chunks (336) 12.2 us, 22 chunks (462) 11.7 us.
   const int64_t span = kGK;
-  // (at most 32 splits: the finisher adds every split of an element in turn)
-  int64_t splits = std::max<int64_t>(1, std::min<int64_t>(32, (320 + g.tiles - 1) / g.tiles));
+  // (at most kGMaxSplits: the finisher holds every split of an element at once)
+  int64_t splits = std::max<int64_t>(1, std::min<int64_t>(kGMaxSplits, 256 / g.tiles));
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, cdiv(d_in, span)));
   g.kchunk = cdiv(cdiv(d_in, splits), span) * span;
   g.splits = cdiv(d_in, g.kchunk);
