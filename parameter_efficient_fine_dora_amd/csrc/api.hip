@@ -507,9 +507,13 @@ int forward_impl(const dora_shape* shape, const void* x, const void* W0, const v
   }
 
   // xs = s (x A^T): the down-projection, pre-scaled by s.  It does not depend
-  // on the norm (and uses other workspace regions), so it runs on a side
-  // stream beside the norm's chain and joins before the forward GEMM.
-  SideStream* side = (allow_side_stream && !noT && s.r > 0) ? side_stream() : nullptr;
+  // on the norm (and uses other workspace regions), so on large layers it runs
+  // on a side stream beside the norm's chain and joins before the forward GEMM.
+  // Layers whose forward GEMM is under 128 GFLOP keep it on the caller's stream
+  // after the norm: there the fork and join cost more than the overlap gains.
+  const double fwd_flop = 2.0 * (double)s.tokens * (double)s.d_out * (double)(s.d_in + s.r);
+  SideStream* side =
+      (allow_side_stream && !noT && s.r > 0 && fwd_flop >= 128e9) ? side_stream() : nullptr;
   auto down_proj = [&](hipStream_t on) -> int {
     GemmProblem d;
     d.M = s.tokens;

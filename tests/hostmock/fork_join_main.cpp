@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <map>
 #include <string>
 
@@ -61,6 +62,14 @@ static bool check(const char* what, int rc, hipStream_t caller) {
   return true;
 }
 
+// Whether a launch labelled `label` went to a stream other than the caller's.
+static bool launched_beside(const char* label, hipStream_t caller) {
+  for (const Op& o : mock::log())
+    if (o.kind == Op::kLaunch && o.label == label && o.stream != caller) return true;
+  std::printf("%s did not run on the side stream\n", label);
+  return false;
+}
+
 // Whether every launch labelled `consumer` is ordered after every launch
 // labelled `producer` (same stream and later, or reached through recorded
 // events); true when either label is absent (a failed call stops early).
@@ -101,7 +110,8 @@ static bool ordered_after(const char* consumer, const char* producer) {
 int main() {
   MockStream caller_obj{100};
   hipStream_t caller = &caller_obj;
-  dora_shape s{256, 512, 32, 64, DORA_BF16, 2.0f, 0u, 0u};
+  // large enough that the forward puts the down-projection on the side stream
+  dora_shape s{4096, 4096, 64, 4096, DORA_BF16, 2.0f, 0u, 0u};
   char* fake = reinterpret_cast<char*>(uintptr_t(1) << 20);   // never dereferenced
   bool ok = true;
 
@@ -112,6 +122,8 @@ int main() {
   ok &= ordered_after("fused_fwd_gemm", "down_proj_xs");
   ok &= ordered_after("fused_fwd_gemm", "cross_gram_proj");
   ok &= ordered_after("cross_gram_proj", "gram_finalize");
+  const char* fail = std::getenv("DORA_MOCK_FAIL");
+  if (!fail || !*fail) ok &= launched_beside("down_proj_xs", caller);
 
   mock::log().clear();
   rc = dora_backward(&s, fake, fake, fake, fake, fake, fake, reinterpret_cast<float*>(fake), fake,

@@ -474,11 +474,15 @@ def test_timing_hook(ops):
     assert ops.timing_collect() == {}
 
 
-def test_side_stream_overlap_matches_serial(ops):
-    """The down-projection (forward) and dm, dB (backward) run on a side stream
-    beside the norm and ts; with the timing hook on, everything runs on the
-    caller's stream.  Both orders must give the same bits (no shared buffer)."""
-    shape = LayerShape(520, 1032, 136, 300, 2.0, "bf16")
+@pytest.mark.parametrize("shape", [LayerShape(520, 1032, 136, 300, 2.0, "bf16"),
+                                   LayerShape(4096, 4104, 136, 4096, 2.0, "bf16")],
+                         ids=["small", "large"])
+def test_side_stream_overlap_matches_serial(ops, shape):
+    """The down-projection (forward, when the forward GEMM holds at least 128
+    GFLOP: the large shape) and ts, dm (backward) run on a side stream beside
+    the norm and the compose backward; with the timing hook on, everything runs
+    on the caller's stream.  Both orders must give the same bits (no shared
+    buffer)."""
     layer = synth.make_layer(shape, 17, grad=True)
     outs = []
     for timing in (False, True, False):

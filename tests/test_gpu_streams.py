@@ -19,9 +19,17 @@ import synth
 from synth import LayerShape
 from tests.gpu_util import layer_to_device
 
-pytestmark = pytest.mark.gpu
 
-SHAPE = LayerShape(520, 1032, 136, 300, 2.0, "bf16")
+# The forward forks its down-projection to the side stream only when its GEMM
+# holds at least 128 GFLOP; the second shape is above that, the first below.
+SHAPES = [LayerShape(520, 1032, 136, 300, 2.0, "bf16"),
+          LayerShape(4096, 4104, 136, 4096, 2.0, "bf16")]
+FORK_FLOP = 128e9
+
+
+def test_shapes_cover_both_forward_arrangements():
+    flops = [2.0 * s.tokens * s.d_out * (s.d_in + s.r) for s in SHAPES]
+    assert flops[0] < FORK_FLOP <= flops[1]
 
 
 def say(msg):
@@ -61,8 +69,10 @@ def step(ops, d, o, s):
 OUTS = ("y", "norm", "xs", "gx", "gA", "gB", "gm")
 
 
-def test_graph_capture_replays_to_eager_bits(ops):
-    say("graph capture of forward + backward")
+@pytest.mark.parametrize("SHAPE", SHAPES, ids=["small", "large"])
+@pytest.mark.gpu
+def test_graph_capture_replays_to_eager_bits(ops, SHAPE):
+    say(f"graph capture of forward + backward {SHAPE}")
     layer = synth.make_layer(SHAPE, 61, grad=True)
     d = layer_to_device(layer, "bf16")
     eager = buffers(ops, SHAPE, "cuda")
@@ -94,8 +104,10 @@ def test_graph_capture_replays_to_eager_bits(ops):
             assert torch.equal(eager[k], ref[k]), (rep, k, "eager")
 
 
-def test_two_host_threads_two_streams(ops):
-    say("two host threads, two streams")
+@pytest.mark.parametrize("SHAPE", SHAPES, ids=["small", "large"])
+@pytest.mark.gpu
+def test_two_host_threads_two_streams(ops, SHAPE):
+    say(f"two host threads, two streams {SHAPE}")
     layer = synth.make_layer(SHAPE, 62, grad=True)
     d = layer_to_device(layer, "bf16")
     serial = buffers(ops, SHAPE, "cuda")
