@@ -691,8 +691,10 @@ DORA_API int dora_backward(const dora_shape* shape, const void* grad_y, const vo
   // beside the compose backward and dB (which need only gz and xs); dx waits
   // for all of them.  dA follows dx on the caller's stream: dx fills the chip in
   // whole rounds of workgroups, and anything beside it only delays its second
-  // round.
-  SideStream* side = (!exact && need_ts) ? side_stream() : nullptr;
+  // round.  Layers whose dx is under 128 GFLOP stay on the caller's stream: there
+  // the fork and join cost more than the overlap gains.
+  const double dx_flop = 2.0 * (double)s.tokens * (double)s.d_in * (double)(s.d_out + s.r);
+  SideStream* side = (!exact && need_ts && dx_flop >= 128e9) ? side_stream() : nullptr;
   SideFork fk(side, st);
   if (side) {
     HIP_TRY(fk.fork());

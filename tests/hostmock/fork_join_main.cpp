@@ -110,7 +110,7 @@ static bool ordered_after(const char* consumer, const char* producer) {
 int main() {
   MockStream caller_obj{100};
   hipStream_t caller = &caller_obj;
-  // large enough that the forward puts the down-projection on the side stream
+  // large enough that the forward and the backward use the side stream
   dora_shape s{4096, 4096, 64, 4096, DORA_BF16, 2.0f, 0u, 0u};
   char* fake = reinterpret_cast<char*>(uintptr_t(1) << 20);   // never dereferenced
   bool ok = true;
@@ -135,6 +135,7 @@ int main() {
   ok &= ordered_after("dx_gemm", "compose_bwd");
   ok &= ordered_after("dA_gemm", "t_proj");
   ok &= ordered_after("dm_finalize", "compose_bwd");
+  if (!fail || !*fail) ok &= launched_beside("t_proj", caller);
   ok &= ordered_after("dB_gemm", "compose_bwd");
   return ok ? 0 : 1;
 }

@@ -478,11 +478,11 @@ def test_timing_hook(ops):
                                    LayerShape(4096, 4104, 136, 4096, 2.0, "bf16")],
                          ids=["small", "large"])
 def test_side_stream_overlap_matches_serial(ops, shape):
-    """The down-projection (forward, when the forward GEMM holds at least 128
-    GFLOP: the large shape) and ts, dm (backward) run on a side stream beside
-    the norm and the compose backward; with the timing hook on, everything runs
-    on the caller's stream.  Both orders must give the same bits (no shared
-    buffer)."""
+    """On the large shape (forward GEMM and dx of at least 128 GFLOP) the
+    down-projection (forward) and ts, dm (backward) run on a side stream beside
+    the norm and the compose backward; with the timing hook on, and on the
+    small shape, everything runs on the caller's stream.  Both orders must give
+    the same bits (no shared buffer)."""
     layer = synth.make_layer(shape, 17, grad=True)
     outs = []
     for timing in (False, True, False):

@@ -21,15 +21,17 @@ from tests.gpu_util import layer_to_device
 
 
 # The forward forks its down-projection to the side stream only when its GEMM
-# holds at least 128 GFLOP; the second shape is above that, the first below.
+# holds at least 128 GFLOP, the backward its ts chain only when dx does; the
+# second shape is above that, the first below.
 SHAPES = [LayerShape(520, 1032, 136, 300, 2.0, "bf16"),
           LayerShape(4096, 4104, 136, 4096, 2.0, "bf16")]
 FORK_FLOP = 128e9
 
 
-def test_shapes_cover_both_forward_arrangements():
-    flops = [2.0 * s.tokens * s.d_out * (s.d_in + s.r) for s in SHAPES]
-    assert flops[0] < FORK_FLOP <= flops[1]
+def test_shapes_cover_both_stream_arrangements():
+    fwd = [2.0 * s.tokens * s.d_out * (s.d_in + s.r) for s in SHAPES]
+    dx = [2.0 * s.tokens * s.d_in * (s.d_out + s.r) for s in SHAPES]
+    assert fwd[0] < FORK_FLOP <= fwd[1] and dx[0] < FORK_FLOP <= dx[1]
 
 
 def say(msg):
