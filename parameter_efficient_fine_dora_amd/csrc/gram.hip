@@ -151,10 +151,11 @@ __global__ __launch_bounds__(256) void dora_gram_partial(const uint16_t* A, int 
 }
 
 // Workgroup (tile, g) finishes rows 4g .. 4g + 3 of an upper-triangle tile: each
-// thread adds one element's split sums in split order (coalesced, every load
-// in flight before the first add; at most kGMaxSplits) and writes the scaled hi + lo pair at (i, j) and at the mirror
-// (j, i).  On a diagonal tile only the elements on or above the diagonal are
-// taken, each written to both places, so G comes out exactly symmetric.
+// thread adds one element's split sums in split order (coalesced, every load in
+// flight before the first add; at most kGMaxSplits splits) and writes the scaled
+// hi + lo pair at (i, j) and at the mirror (j, i).  On a diagonal tile only the
+// elements on or above the diagonal are taken, each written to both places, so
+// G comes out exactly symmetric.
 constexpr int kGFinRows = 4;
 constexpr int kGMaxSplits = 32;
 __global__ __launch_bounds__(256) void dora_gram_finish(const float* part, int splits, int r,
